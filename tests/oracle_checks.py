@@ -1,0 +1,297 @@
+"""Pins for the fp64 oracle: checks against closed forms, library routines and
+exact arithmetic, written as functions of the implementation under test.
+
+Each check raises AssertionError when the implementation disagrees with what
+the pages and the mathematics fix. The oracle must pass all of them; the
+mutation tests run the same checks on deliberately broken variants (a dropped
+lambda, swapped weights, a wrong GQA map, a wrong scale, an off-by-one mask,
+a log2 lse) and require that some check fails for each.
+
+Sources: YOCO++ technical summary, section 2 (KV composition equations;
+key technical innovations items 2-3: lambda = 35, initialisation
+alpha_1 = 0, alpha_2 = 1/lambda); YOCO summary, abstract (cross-decoder
+reuses the global cache; behaves like a decoder-only Transformer; early exit
+leaves the output unchanged).
+"""
+from __future__ import annotations
+
+from decimal import Decimal, getcontext
+
+import numpy as np
+import torch
+
+from synthetic import inputs as S
+
+LAM = 35.0
+INV_LAM32 = S.fl32(1.0 / LAM)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _f64(x):
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return S.bf16_bits_to_f32(x).astype(np.float64)
+    return x.astype(np.float64)
+
+
+# ----------------------------------------------------------------- compose
+
+def _pair(dtype, shape=(2, 19, 3, 64), seed=11):
+    r = _rng(seed)
+    a = r.standard_normal(shape).astype(np.float32)
+    b = r.standard_normal(shape).astype(np.float32)
+    if dtype == "bf16":
+        return S.f32_to_bf16_bits(a), S.f32_to_bf16_bits(b)
+    return a, b
+
+
+def check_compose_identity(compose_fn, dtype="f32"):
+    """Init alpha_1 = 0, alpha_2 = fl32(1/35): stored K'_i must equal K_i exactly."""
+    k1, ki = _pair(dtype)
+    r = np.asarray(compose_fn(k1, ki, 0.0, INV_LAM32), dtype=np.float64)
+    want = _f64(ki)
+    # fp64 value is K_i * 35 * fl32(1/35) = K_i * (1 + 5.6e-9): below half an
+    # fp32 ulp, so the stored value rounds back to K_i.
+    nz = want != 0
+    assert np.all(np.abs(r[nz] / want[nz] - 1.0) < 1e-8)
+    if dtype == "f32":
+        assert np.array_equal(r.astype(np.float32), ki)
+    else:
+        assert np.array_equal(S.f32_to_bf16_bits(r.astype(np.float32)), ki)
+
+
+def check_compose_mirror(compose_fn, dtype="f32"):
+    """alpha_1 = fl32(1/35), alpha_2 = 0 stores layer 1's tensor."""
+    k1, ki = _pair(dtype, seed=12)
+    r = np.asarray(compose_fn(k1, ki, INV_LAM32, 0.0), dtype=np.float64)
+    if dtype == "f32":
+        assert np.array_equal(r.astype(np.float32), k1)
+    else:
+        assert np.array_equal(S.f32_to_bf16_bits(r.astype(np.float32)), k1)
+
+
+def check_compose_integer_closed_form(compose_fn):
+    """lam = 2, a1 = 1.5, a2 = -0.25 on small integers: exactly 3*X1 - 0.5*Xi."""
+    r = _rng(13)
+    x1 = r.integers(-8, 9, size=(1, 7, 2, 8)).astype(np.float32)
+    xi = r.integers(-8, 9, size=(1, 7, 2, 8)).astype(np.float32)
+    got = np.asarray(compose_fn(x1, xi, 1.5, -0.25, 2.0), dtype=np.float64)
+    assert np.array_equal(got, 3.0 * x1.astype(np.float64) - 0.5 * xi.astype(np.float64))
+    # and with the page's lambda: 35 * (0.5 * X1 + 0.25 * Xi) = 17.5 X1 + 8.75 Xi exactly
+    got = np.asarray(compose_fn(x1, xi, 0.5, 0.25), dtype=np.float64)
+    assert np.array_equal(got, 17.5 * x1.astype(np.float64) + 8.75 * xi.astype(np.float64))
+
+
+def check_compose_kv_weights(compose_kv_fn, dtype="f32"):
+    """Key weights act on K, value weights on V: K identity + V mirror in one call."""
+    k1, ki = _pair(dtype, seed=14)
+    v1, vi = _pair(dtype, seed=15)
+    ident, mirror = (0.0, INV_LAM32), (INV_LAM32, 0.0)
+    for ka, kw in ((ident, ki), (mirror, k1)):
+        for va, vw in ((ident, vi), (mirror, v1)):
+            kp, vp = compose_kv_fn(k1, ki, v1, vi, ka + va)
+            if dtype == "f32":
+                assert np.array_equal(np.asarray(kp).astype(np.float32), kw)
+                assert np.array_equal(np.asarray(vp).astype(np.float32), vw)
+            else:
+                assert np.array_equal(S.f32_to_bf16_bits(np.asarray(kp).astype(np.float32)), kw)
+                assert np.array_equal(S.f32_to_bf16_bits(np.asarray(vp).astype(np.float32)), vw)
+
+
+# ----------------------------------------------------------------- decode
+
+def _qkv(B, Hq, Hkv, T, D, seed):
+    r = _rng(seed)
+    q = r.standard_normal((B, Hq, D))
+    k = r.standard_normal((B, Hkv, T, D))
+    v = r.standard_normal((B, Hkv, T, D))
+    return q, k, v
+
+
+def check_decode_identical_keys(decode_fn):
+    """All keys equal: weights are uniform, o = mean_t V, lse = s + ln T."""
+    B, Hq, Hkv, T, D = 2, 4, 2, 37, 8
+    q, k, v = _qkv(B, Hq, Hkv, T, D, 21)
+    k[:] = k[:, :, :1, :]
+    o, lse = decode_fn(q, k, v)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            assert np.allclose(o[b, h], v[b, g].mean(axis=0), rtol=0, atol=1e-13)
+            s = (q[b, h] @ k[b, g, 0]) / np.sqrt(D)
+            assert abs(lse[b, h] - (s + np.log(T))) < 1e-12
+
+
+def check_decode_single_token(decode_fn):
+    """T = 1: o = V[0] exactly, lse = the single score."""
+    q, k, v = _qkv(2, 4, 1, 1, 16, 22)
+    o, lse = decode_fn(q, k, v)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(o[b, h], v[b, 0, 0])
+            assert abs(lse[b, h] - q[b, h] @ k[b, 0, 0] / 4.0) < 1e-13
+
+
+def check_decode_constant_values(decode_fn):
+    """All value rows equal c: o = c whatever the keys."""
+    q, k, v = _qkv(1, 8, 2, 50, 8, 23)
+    k *= 5.0
+    v[:] = v[:, :, :1, :]
+    o, _ = decode_fn(q, k, v)
+    for h in range(8):
+        assert np.allclose(o[0, h], v[0, h // 4, 0], rtol=0, atol=1e-13)
+
+
+def sdpa_reference(q, k, v, seq_lens=None):
+    """torch fp64 scaled_dot_product_attention on CPU (library routine), GQA by
+    repeat_interleave, one query per sequence."""
+    B, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    o = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        n = k.shape[2] if seq_lens is None else int(seq_lens[b])
+        kk = torch.from_numpy(np.ascontiguousarray(k[b, :, :n])).repeat_interleave(G, dim=0)
+        vv = torch.from_numpy(np.ascontiguousarray(v[b, :, :n])).repeat_interleave(G, dim=0)
+        qq = torch.from_numpy(np.ascontiguousarray(q[b]))[:, None, :]
+        ob = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)
+        o[b] = ob[:, 0].numpy()
+        sc = (qq @ kk.transpose(1, 2))[:, 0, :] / np.sqrt(D)
+        lse[b] = torch.logsumexp(sc, dim=-1).numpy()
+    return o, lse
+
+
+def check_decode_vs_sdpa(decode_fn):
+    """Tiny shapes against torch's fp64 SDPA (with GQA via repeat_interleave)."""
+    for (B, Hq, Hkv, T, D, seed) in [(1, 4, 1, 5, 2, 31), (2, 8, 2, 64, 8, 32), (3, 6, 3, 33, 64, 33),
+                                     (1, 2, 2, 17, 8, 34)]:
+        q, k, v = _qkv(B, Hq, Hkv, T, D, seed)
+        k[:, 1 % Hkv] *= 3.0  # make kv heads clearly different
+        o, lse = decode_fn(q, k, v)
+        o_ref, lse_ref = sdpa_reference(q, k, v)
+        assert np.allclose(o, o_ref, rtol=0, atol=1e-12)
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def check_decode_seq_lens(decode_fn):
+    """Rows at or beyond seq_lens[b] never matter (fill them with garbage)."""
+    q, k, v = _qkv(3, 4, 2, 40, 8, 35)
+    lens = np.array([40, 1, 23])
+    k2, v2 = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        k2[b, :, n:] = 1e3
+        v2[b, :, n:] = -7e2
+    o, lse = decode_fn(q, k2, v2, seq_lens=lens)
+    o_ref, lse_ref = sdpa_reference(q, k, v, seq_lens=lens)
+    assert np.allclose(o, o_ref, rtol=0, atol=1e-12)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def check_decode_decimal(decode_fn):
+    """T = 3, D = 2 against a 50-digit Decimal evaluation of the definition."""
+    getcontext().prec = 50
+    r = _rng(36)
+    q = np.round(r.standard_normal((1, 2, 2)), 3)
+    k = np.round(r.standard_normal((1, 1, 3, 2)) * 2, 3)
+    v = np.round(r.standard_normal((1, 1, 3, 2)), 3)
+    o, lse = decode_fn(q, k, v)
+    sc = Decimal(1) / Decimal(2).sqrt()
+    for h in range(2):
+        qs = [Decimal(repr(float(x))) for x in q[0, h]]
+        s = [sc * sum(qs[d] * Decimal(repr(float(k[0, 0, t, d]))) for d in range(2)) for t in range(3)]
+        e = [x.exp() for x in s]
+        tot = sum(e)
+        for d in range(2):
+            od = sum(e[t] * Decimal(repr(float(v[0, 0, t, d]))) for t in range(3)) / tot
+            assert abs(Decimal(repr(float(o[0, h, d]))) - od) < Decimal("1e-14")
+        assert abs(Decimal(repr(float(lse[0, h]))) - tot.ln()) < Decimal("1e-14")
+
+
+def check_decode_planted_row(decode_fn):
+    """A key row equal to 4*q (score 4|q|^2/sqrt(D)) takes nearly all the weight."""
+    B, Hq, Hkv, T, D = 1, 4, 1, 4096, 128
+    q, k, v = _qkv(B, Hq, Hkv, T, D, 37)
+    t_star = 1234
+    k[0, 0, t_star] = 4.0 * q[0, 0]
+    o, _ = decode_fn(q, k, v)
+    assert np.max(np.abs(o[0, 0] - v[0, 0, t_star])) < 1e-6
+
+
+DECODE_CHECKS = [check_decode_identical_keys, check_decode_single_token, check_decode_constant_values,
+                 check_decode_vs_sdpa, check_decode_seq_lens, check_decode_decimal, check_decode_planted_row]
+
+
+# ----------------------------------------------------------------- prefill
+
+def sdpa_causal_reference(q, k, v, p0):
+    """torch fp64 SDPA with an explicit causal mask at offset p0 (library routine)."""
+    B, C, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    n = p0 + C
+    o = np.empty((B, C, Hq, D))
+    for b in range(B):
+        kk = torch.from_numpy(np.ascontiguousarray(k[b, :, :n])).repeat_interleave(G, dim=0)
+        vv = torch.from_numpy(np.ascontiguousarray(v[b, :, :n])).repeat_interleave(G, dim=0)
+        qq = torch.from_numpy(np.ascontiguousarray(q[b].transpose(1, 0, 2)))   # [Hq, C, D]
+        mask = torch.arange(n)[None, :] <= (p0 + torch.arange(C))[:, None]
+        if p0 == 0:
+            ob = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True)
+        else:
+            ob = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask)
+        o[b] = ob.numpy().transpose(1, 0, 2)
+    return o
+
+
+def _prefill_inputs(B, C, Hq, Hkv, Tcap, D, seed):
+    r = _rng(seed)
+    return (r.standard_normal((B, C, Hq, D)), r.standard_normal((B, Hkv, Tcap, D)),
+            r.standard_normal((B, Hkv, Tcap, D)))
+
+
+def check_prefill_first_row(prefill_fn):
+    """p0 = 0: the first query sees only row 0, so o = V[0] exactly."""
+    q, k, v = _prefill_inputs(2, 9, 4, 2, 9, 16, 41)
+    o, lse = prefill_fn(q, k, v, 0)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(o[b, 0, h], v[b, h // 2, 0])
+
+
+def check_prefill_vs_sdpa(prefill_fn):
+    for (B, C, Hq, Hkv, Tcap, D, p0, seed) in [(1, 16, 4, 1, 16, 8, 0, 42), (2, 7, 4, 2, 30, 8, 11, 43),
+                                               (1, 33, 8, 2, 40, 64, 0, 44), (1, 5, 2, 1, 12, 2, 7, 45)]:
+        q, k, v = _prefill_inputs(B, C, Hq, Hkv, Tcap, D, seed)
+        o, _ = prefill_fn(q, k, v, p0)
+        assert np.allclose(o, sdpa_causal_reference(q, k, v, p0), rtol=0, atol=1e-12)
+
+
+def check_prefill_row_is_decode(prefill_fn, decode_fn):
+    """Row at position p equals a decode over the first p+1 rows (and the last
+    row of the chunk equals decode at T = p0 + C: early exit changes nothing)."""
+    B, C, Hq, Hkv, D, p0 = 2, 12, 4, 2, 8, 5
+    q, k, v = _prefill_inputs(B, C, Hq, Hkv, p0 + C + 3, D, 46)
+    o, lse = prefill_fn(q, k, v, p0)
+    for c in range(C):
+        od, ld = decode_fn(q[:, c], k, v, seq_lens=np.full(B, p0 + c + 1))
+        assert np.allclose(o[:, c], od, rtol=0, atol=1e-13)
+        assert np.allclose(lse[:, :, c], ld, rtol=0, atol=1e-13)
+
+
+def check_prefill_chunk_independence(prefill_fn):
+    """Chunking only partitions query rows: one call over all rows equals the
+    concatenation of chunked calls."""
+    B, T, Hq, Hkv, D = 1, 24, 4, 1, 8
+    q, k, v = _prefill_inputs(B, T, Hq, Hkv, T, D, 47)
+    full, full_lse = prefill_fn(q, k, v, 0)
+    for c0 in range(0, T, 7):
+        c1 = min(T, c0 + 7)
+        part, part_lse = prefill_fn(q[:, c0:c1], k, v, c0)
+        assert np.allclose(part, full[:, c0:c1], rtol=0, atol=1e-13)
+        assert np.allclose(part_lse, full_lse[:, :, c0:c1], rtol=0, atol=1e-13)
+
+
+PREFILL_CHECKS = [check_prefill_first_row, check_prefill_vs_sdpa, check_prefill_chunk_independence]
