@@ -1,0 +1,54 @@
+// Shared host/device definitions of the gfx950 HIP path (no oracle code here).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace yoco {
+
+// Device view of a 4-D tensor: element (b, h, t, 0) at ptr + b*sb + h*sh + t*st.
+struct View4 {
+  const void* ptr;
+  int64_t sb, sh, st;
+};
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipSuccess or the error of the launch (hipGetLastError).
+
+struct ComposeParams {
+  View4 k1, ki, v1, vi;  // sources, rows [0, n)
+  View4 kc, vc;          // caches, rows [t0, t0 + n)
+  int t0, B, n, Hkv, D;
+  float cK1, cK2, cV1, cV2;  // lambda folded into the weights (fp32)
+};
+hipError_t launch_compose(const ComposeParams& p, bool bf16, hipStream_t stream);
+
+struct DecodeParams {
+  const void* q;          // [B, Hq, D]
+  View4 k, v;             // caches
+  const int32_t* seq_lens;
+  int B, T, Hq, Hkv, D;
+  float scale_log2;       // softmax scale * log2(e)
+  int num_splits;
+  int rows_per_split;
+  float* out;             // [B, Hq, D] (used when num_splits == 1)
+  float* lse;             // [B, Hq] or null (used when num_splits == 1)
+  float* part_o;          // [B, Hq, S, D]   (used when num_splits > 1)
+  float* part_lse;        // [B, Hq, S]
+};
+hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_decode_merge(const float* part_o, const float* part_lse, int B, int Hq, int D, int S,
+                               float* out, float* lse, hipStream_t stream);
+
+struct PrefillParams {
+  const void* q;   // [B, C, Hq, D] bf16
+  View4 k, v;      // bf16 caches
+  int B, C, p0, Hq, Hkv, D;
+  float scale_log2;
+  void* out;       // [B, C, Hq, D]
+  bool out_bf16;
+  float* lse;      // [B, Hq, C] or null
+};
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+}  // namespace yoco

@@ -1,0 +1,164 @@
+// Composition of a lower-half layer's cached KVs, written straight into the
+// cache (YOCO++ technical summary, section 2, KV composition equations; key
+// technical innovation 1: the composed K', V' are what is cached).
+//
+//   X'_i = c1 * X_1 + c2 * X_i,  c1 = fl32(lambda * a1), c2 = fl32(lambda * a2)
+//
+// computed as fma(c2, X_i, c1 * X_1) in fp32 and rounded once to the cache
+// dtype. A zero weight drops its term (and its read): with the YOCO
+// initialisation (a1 = 0, a2 = 1/lambda) the result is X_i bit for bit.
+//
+// HBM-bound (0.5 flop per byte in bf16): every thread moves 16-byte vectors,
+// K and V of the same position are handled by the same thread in one launch,
+// and each thread keeps UNROLL independent positions in flight.
+
+#include "common.h"
+
+namespace yoco {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Which terms are present: 3 = both, 2 = only X_i, 1 = only X_1, 0 = none (zeros).
+template <bool BF16, int TERMS>
+__device__ __forceinline__ u32x4 combine(u32x4 x1, u32x4 xi, float c1, float c2) {
+  uint32_t a[4] = {x1[0], x1[1], x1[2], x1[3]};
+  uint32_t b[4] = {xi[0], xi[1], xi[2], xi[3]};
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (BF16) {
+      float l, h;
+      if constexpr (TERMS == 3) {
+        l = __builtin_fmaf(c2, lo_bf16(b[j]), c1 * lo_bf16(a[j]));
+        h = __builtin_fmaf(c2, hi_bf16(b[j]), c1 * hi_bf16(a[j]));
+      } else if constexpr (TERMS == 2) {
+        l = c2 * lo_bf16(b[j]);
+        h = c2 * hi_bf16(b[j]);
+      } else if constexpr (TERMS == 1) {
+        l = c1 * lo_bf16(a[j]);
+        h = c1 * hi_bf16(a[j]);
+      } else {
+        l = 0.f;
+        h = 0.f;
+      }
+      r[j] = pack_bf16(l, h);
+    } else {
+      float y;
+      if constexpr (TERMS == 3) {
+        y = __builtin_fmaf(c2, __uint_as_float(b[j]), c1 * __uint_as_float(a[j]));
+      } else if constexpr (TERMS == 2) {
+        y = c2 * __uint_as_float(b[j]);
+      } else if constexpr (TERMS == 1) {
+        y = c1 * __uint_as_float(a[j]);
+      } else {
+        y = 0.f;
+      }
+      r[j] = __float_as_uint(y);
+    }
+  }
+  u32x4 out = {r[0], r[1], r[2], r[3]};
+  return out;
+}
+
+struct Args {
+  ComposeParams p;
+  uint32_t cpr;     // 16-byte chunks per row (D * elemsize / 16)
+  uint32_t total;   // B * n * Hkv * cpr
+  int esize;        // bytes per element
+};
+
+__device__ __forceinline__ const u32x4* at(const View4& v, int b, int h, int t, uint32_t c, int es) {
+  const char* base = static_cast<const char*>(v.ptr);
+  int64_t e = (int64_t)b * v.sb + (int64_t)h * v.sh + (int64_t)t * v.st;
+  return reinterpret_cast<const u32x4*>(base + e * es) + c;
+}
+
+template <bool BF16, int TK, int TV>
+__global__ __launch_bounds__(kThreads) void compose_kernel(Args a) {
+  const ComposeParams& p = a.p;
+  u32x4 k1[kUnroll] = {}, ki[kUnroll] = {}, v1[kUnroll] = {}, vi[kUnroll] = {};
+  uint32_t idx[kUnroll];
+  const uint32_t base = (uint32_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+
+  // Issue every load of the UNROLL positions first, then combine and store.
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    idx[u] = base + u * kThreads;
+    if (idx[u] >= a.total) continue;
+    uint32_t c = idx[u] % a.cpr;
+    uint32_t r = idx[u] / a.cpr;
+    int h = (int)(r % (uint32_t)p.Hkv);
+    r /= (uint32_t)p.Hkv;
+    int t = (int)(r % (uint32_t)p.n);
+    int b = (int)(r / (uint32_t)p.n);
+    if constexpr (TK & 1) k1[u] = __builtin_nontemporal_load(at(p.k1, b, h, t, c, a.esize));
+    if constexpr (TK & 2) ki[u] = __builtin_nontemporal_load(at(p.ki, b, h, t, c, a.esize));
+    if constexpr (TV & 1) v1[u] = __builtin_nontemporal_load(at(p.v1, b, h, t, c, a.esize));
+    if constexpr (TV & 2) vi[u] = __builtin_nontemporal_load(at(p.vi, b, h, t, c, a.esize));
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if (idx[u] >= a.total) continue;
+    uint32_t c = idx[u] % a.cpr;
+    uint32_t r = idx[u] / a.cpr;
+    int h = (int)(r % (uint32_t)p.Hkv);
+    r /= (uint32_t)p.Hkv;
+    int t = (int)(r % (uint32_t)p.n);
+    int b = (int)(r / (uint32_t)p.n);
+    u32x4 ko = combine<BF16, TK>(k1[u], ki[u], p.cK1, p.cK2);
+    u32x4 vo = combine<BF16, TV>(v1[u], vi[u], p.cV1, p.cV2);
+    __builtin_nontemporal_store(ko, const_cast<u32x4*>(at(p.kc, b, h, p.t0 + t, c, a.esize)));
+    __builtin_nontemporal_store(vo, const_cast<u32x4*>(at(p.vc, b, h, p.t0 + t, c, a.esize)));
+  }
+}
+
+template <bool BF16, int TK>
+hipError_t dispatch_v(const Args& a, int tv, dim3 grid, hipStream_t s) {
+  switch (tv) {
+    case 0: compose_kernel<BF16, TK, 0><<<grid, kThreads, 0, s>>>(a); break;
+    case 1: compose_kernel<BF16, TK, 1><<<grid, kThreads, 0, s>>>(a); break;
+    case 2: compose_kernel<BF16, TK, 2><<<grid, kThreads, 0, s>>>(a); break;
+    default: compose_kernel<BF16, TK, 3><<<grid, kThreads, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t dispatch(const Args& a, int tk, int tv, dim3 grid, hipStream_t s) {
+  switch (tk) {
+    case 0: return dispatch_v<BF16, 0>(a, tv, grid, s);
+    case 1: return dispatch_v<BF16, 1>(a, tv, grid, s);
+    case 2: return dispatch_v<BF16, 2>(a, tv, grid, s);
+    default: return dispatch_v<BF16, 3>(a, tv, grid, s);
+  }
+}
+
+int terms(float c1, float c2) { return (c1 != 0.f ? 1 : 0) | (c2 != 0.f ? 2 : 0); }
+
+}  // namespace
+
+hipError_t launch_compose(const ComposeParams& p, bool bf16, hipStream_t stream) {
+  Args a;
+  a.p = p;
+  a.esize = bf16 ? 2 : 4;
+  a.cpr = (uint32_t)(p.D * a.esize / 16);
+  a.total = (uint32_t)((uint64_t)p.B * p.n * p.Hkv * a.cpr);
+  dim3 grid((a.total + kThreads * kUnroll - 1) / (kThreads * kUnroll));
+  int tk = terms(p.cK1, p.cK2), tv = terms(p.cV1, p.cV2);
+  return bf16 ? dispatch<true>(a, tk, tv, grid, stream) : dispatch<false>(a, tk, tv, grid, stream);
+}
+
+}  // namespace yoco

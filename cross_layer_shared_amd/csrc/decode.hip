@@ -1,0 +1,402 @@
+// Decode attention of the cross-decoder over the one shared cache
+// (YOCO summary, abstract and method details: every cross-decoder layer
+// reuses the global KV cache via cross-attention; YOCO++ summary, section 2:
+// the cache is the middle layer's composed K'_{L/2}, V'_{L/2}; section 3:
+// decoding reads exactly one KV set per layer).
+//
+// Split pass: one workgroup (4 wavefronts) per (sequence b, kv head g,
+// split s) streams the split's rows of K' and V' exactly once. The G = Hq/Hkv
+// query heads that share kv head g are all served from the same loaded row.
+//
+// Lane layout of a wavefront: the 64 lanes form four 16-lane DPP rows
+// ("groups"); in one iteration group j holds cache rows base + 4u + j for
+// u < U = 16/G, lane s of the group holding elements [s*D/16, (s+1)*D/16) of
+// each row. One load instruction of the wavefront therefore reads four
+// consecutive cache rows: a contiguous 1 KiB block for a bf16 D=128 cache.
+//
+// Scores: each lane forms the 16 = U*G partial dot products over its slice,
+// and a transposed butterfly over the 16 lanes of the group (DPP partners
+// s^8, s^7, s^2, s^1, which span the 4 lane bits) leaves lane s holding the
+// complete score of (row u, head hh) with s = u*G + hh. Each group keeps an
+// online-softmax state (running max m and sum l per head, in the log2
+// domain, and the weighted value sums of its slice); the running max only
+// rescales the value sums when some lane's maximum grew. The four groups and
+// four wavefronts merge their states once per split.
+//
+// Merge pass: the splits' normalised outputs are combined with their
+// log-sum-exps.
+
+#include <math.h>
+
+#include "common.h"
+
+namespace yoco {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---- DPP helpers (within 16-lane rows) ----
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kHalfMirror = 0x141;    // row_half_mirror: lane ^ 7 within 8
+constexpr int kRowRor = 0x120;        // + n: rotate right by n within the row
+constexpr int kRowNewBcast = 0x150;   // + n: broadcast lane n of each row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Broadcast lane n (compile-time) of each 16-lane row to the whole row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp<kRowNewBcast + N>(x);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int N>
+struct DW {
+  typedef uint32_t type __attribute__((ext_vector_type(N)));
+};
+template <>
+struct DW<1> {
+  typedef uint32_t type;
+};
+
+template <bool BF16, int D>
+struct Layout {
+  static constexpr int kEPL = D / 16;                       // elements per lane per row
+  static constexpr int kNDW = BF16 ? kEPL / 2 : kEPL;       // dwords per lane per row
+  static constexpr int kES = BF16 ? 2 : 4;                  // bytes per element
+  typedef typename DW<kNDW>::type vec;
+};
+
+template <int N>
+__device__ __forceinline__ uint32_t dw_at(const typename DW<N>::type& v, int i) {
+  if constexpr (N == 1) {
+    return v;
+  } else {
+    return v[i];
+  }
+}
+
+// Transposed butterfly: x[16] partial sums on the 16 lanes of a row ->
+// the lane s returns the full sum of value index s.
+__device__ __forceinline__ float reduce16_transposed(const float (&x)[16], int s) {
+  float y8[8], y4[4], y2[2];
+  const bool b3 = s & 8, b2 = s & 4, b1 = s & 2, b0 = s & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float keep = b3 ? x[i + 8] : x[i];
+    float send = b3 ? x[i] : x[i + 8];
+    y8[i] = keep + dpp<kRowRor + 8>(send);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float keep = b2 ? y8[i + 4] : y8[i];
+    float send = b2 ? y8[i] : y8[i + 4];
+    y4[i] = keep + dpp<kHalfMirror>(send);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float keep = b1 ? y4[i + 2] : y4[i];
+    float send = b1 ? y4[i] : y4[i + 2];
+    y2[i] = keep + dpp<kQuadSwap2>(send);
+  }
+  float keep = b0 ? y2[1] : y2[0];
+  float send = b0 ? y2[0] : y2[1];
+  return keep + dpp<kQuadSwap1>(send);
+}
+
+// All-reduce (max or sum) over the lanes of a row that share s mod G.
+template <int G, bool MAX>
+__device__ __forceinline__ float reduce_same_head(float x) {
+  if constexpr (G <= 1) x = MAX ? fmaxf(x, dpp<kRowRor + 1>(x)) : x + dpp<kRowRor + 1>(x);
+  if constexpr (G <= 2) x = MAX ? fmaxf(x, dpp<kRowRor + 2>(x)) : x + dpp<kRowRor + 2>(x);
+  if constexpr (G <= 4) x = MAX ? fmaxf(x, dpp<kRowRor + 4>(x)) : x + dpp<kRowRor + 4>(x);
+  if constexpr (G <= 8) x = MAX ? fmaxf(x, dpp<kRowRor + 8>(x)) : x + dpp<kRowRor + 8>(x);
+  return x;
+}
+
+template <int I, int N>
+struct Unroll {
+  template <typename F>
+  __device__ __forceinline__ static void run(F&& f) {
+    f.template operator()<I>();
+    Unroll<I + 1, N>::run(f);
+  }
+};
+template <int N>
+struct Unroll<N, N> {
+  template <typename F>
+  __device__ __forceinline__ static void run(F&&) {}
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+  using L = Layout<BF16, D>;
+  using vec = typename L::vec;
+  constexpr int EPL = L::kEPL;
+  constexpr int NDW = L::kNDW;
+  constexpr int U = 16 / G;          // rows per group per iteration
+  constexpr int R = 4 * U;           // rows per wavefront per iteration
+
+  __shared__ float sm_acc[kWaves][G][D];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane >> 4;
+  const int s = lane & 15;
+  const int my_u = s / G;            // row of the score this lane owns
+
+  int len = p.T;
+  if (p.seq_lens) {
+    len = p.seq_lens[b];
+    len = len < 1 ? 1 : (len > p.T ? p.T : len);
+  }
+  const int ts = split * p.rows_per_split;
+  const int te = min(ts + p.rows_per_split, len);
+
+  // Query slices of the G heads of this group (same dims as the lane's K slice).
+  vec qv[G];
+  const char* qbase = static_cast<const char*>(p.q) + ((size_t)(b * p.Hq + g * G) * D + s * EPL) * L::kES;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) qv[hh] = *reinterpret_cast<const vec*>(qbase + (size_t)hh * D * L::kES);
+
+  float acc[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+  float m_run = -INFINITY;   // running max (log2 domain) of head my_h in this group
+  float l_run = 0.f;         // this lane's share of the running sum
+
+  const char* kbase = static_cast<const char*>(p.k.ptr) + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh) * L::kES +
+                      s * EPL * L::kES;
+  const char* vbase = static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh) * L::kES +
+                      s * EPL * L::kES;
+  const int64_t kst = p.k.st * L::kES, vst = p.v.st * L::kES;
+
+  for (int base = ts + wave * R; base < te; base += kWaves * R) {
+    vec kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int row = min(base + 4 * u + j, te - 1);
+      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(kbase + row * kst));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int row = min(base + 4 * u + j, te - 1);
+      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(vbase + row * vst));
+    }
+
+    // Partial dot products over this lane's slice: x[u*G + hh].
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < NDW; ++w) {
+          uint32_t kw = dw_at<NDW>(kr[u], w), qw = dw_at<NDW>(qv[hh], w);
+          if constexpr (BF16) {
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw), __builtin_bit_cast(bf16x2_t, kw), a,
+                                                false);
+          } else {
+            a = __builtin_fmaf(__uint_as_float(qw), __uint_as_float(kw), a);
+          }
+        }
+        x[u * G + hh] = a;
+      }
+    }
+    float sc = reduce16_transposed(x, s) * p.scale_log2;
+    if (base + 4 * my_u + j >= te) sc = -INFINITY;
+
+    float mt = reduce_same_head<G, true>(sc);
+    float m_new = fmaxf(m_run, mt);
+    float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    float pr = fast_exp2(sc - m_use);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+      float alpha = fast_exp2(m_run - m_use);
+      l_run *= alpha;
+      Unroll<0, G>::run([&]<int HH>() {
+        float ah = row_bcast<HH>(alpha);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[HH][e] *= ah;
+      });
+    }
+    m_run = m_new;
+    l_run += pr;
+
+    // acc[hh] += p(u, hh) * V[u] for the U rows of this group.
+    Unroll<0, 16>::run([&]<int V>() {
+      constexpr int u = V / G, hh = V % G;
+      float pv = row_bcast<V>(pr);
+#pragma unroll
+      for (int w = 0; w < NDW; ++w) {
+        uint32_t vw = dw_at<NDW>(vr[u], w);
+        if constexpr (BF16) {
+          acc[hh][2 * w] = __builtin_fmaf(pv, lo_bf16(vw), acc[hh][2 * w]);
+          acc[hh][2 * w + 1] = __builtin_fmaf(pv, hi_bf16(vw), acc[hh][2 * w + 1]);
+        } else {
+          acc[hh][w] = __builtin_fmaf(pv, __uint_as_float(vw), acc[hh][w]);
+        }
+      }
+    });
+  }
+
+  // ---- merge the four groups of the wavefront ----
+  float l_h = reduce_same_head<G, false>(l_run);   // group's sum for head my_h
+  float mg[G], lg[G];
+  Unroll<0, G>::run([&]<int HH>() {
+    mg[HH] = row_bcast<HH>(m_run);
+    lg[HH] = row_bcast<HH>(l_h);
+  });
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float M = fmaxf(mg[hh], __shfl_xor(mg[hh], 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    float w = (mg[hh] == -INFINITY) ? 0.f : fast_exp2(mg[hh] - M);
+    float lw = lg[hh] * w;
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float a = acc[hh][e] * w;
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      acc[hh][e] = a;
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_acc[wave][hh][s * EPL + e] = acc[hh][e];
+      if (s == 0) {
+        sm_m[wave][hh] = M;
+        sm_l[wave][hh] = lw;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the wavefronts and write this split's result ----
+  const int h0 = g * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int hh = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][hh]);
+    float Lsum = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      float m = sm_m[w][hh];
+      float wt = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+      Lsum += wt * sm_l[w][hh];
+      O += wt * sm_acc[w][hh][d];
+    }
+    const bool empty = !(Lsum > 0.f);
+    const float o = empty ? 0.f : O / Lsum;
+    const float lse = empty ? -INFINITY : (M + __log2f(Lsum)) * 0.69314718055994530942f;
+    const int h = h0 + hh;
+    if (p.num_splits == 1) {
+      p.out[((size_t)b * p.Hq + h) * D + d] = o;
+      if (p.lse && d == 0) p.lse[(size_t)b * p.Hq + h] = lse;
+    } else {
+      const size_t row = ((size_t)b * p.Hq + h) * p.num_splits + split;
+      p.part_o[row * D + d] = o;
+      if (d == 0) p.part_lse[row] = lse;
+    }
+  }
+}
+
+// One workgroup (4 wavefronts) per (b, h): wavefront w takes splits w, w+4, ...;
+// lanes run over the head dimension.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                                const float* __restrict__ part_lse, int S,
+                                                                float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int PER = D / 64;
+  __shared__ float red[kWaves];
+  __shared__ float sm_o[kWaves][D];
+  __shared__ float sm_l[kWaves];
+  const int bh = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* pl = part_lse + (size_t)bh * S;
+  const float* po = part_o + (size_t)bh * S * D;
+
+  float M = -INFINITY;
+  for (int i = threadIdx.x; i < S; i += kThreads) M = fmaxf(M, pl[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  float wsum = 0.f;
+#pragma unroll 4
+  for (int i = wave; i < S; i += kWaves) {
+    const float li = pl[i];
+    const float w = (li == -INFINITY) ? 0.f : __expf(li - M);
+    wsum += w;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(w, po[(size_t)i * D + lane + 64 * k], o[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) sm_o[wave][lane + 64 * k] = o[k];
+  if (lane == 0) sm_l[wave] = wsum;
+  __syncthreads();
+  const float L = sm_l[0] + sm_l[1] + sm_l[2] + sm_l[3];
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float v = sm_o[0][d] + sm_o[1][d] + sm_o[2][d] + sm_o[3][d];
+    out[(size_t)bh * D + d] = v / L;
+  }
+  if (lse && threadIdx.x == 0) lse[bh] = M + logf(L);
+}
+
+template <bool BF16, int D>
+hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
+  dim3 grid(p.num_splits, p.Hkv, p.B);
+  switch (p.Hq / p.Hkv) {
+    case 1: decode_split_kernel<BF16, D, 1><<<grid, kThreads, 0, s>>>(p); break;
+    case 2: decode_split_kernel<BF16, D, 2><<<grid, kThreads, 0, s>>>(p); break;
+    case 4: decode_split_kernel<BF16, D, 4><<<grid, kThreads, 0, s>>>(p); break;
+    case 8: decode_split_kernel<BF16, D, 8><<<grid, kThreads, 0, s>>>(p); break;
+    case 16: decode_split_kernel<BF16, D, 16><<<grid, kThreads, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream) {
+  if (bf16) return p.D == 64 ? launch_g<true, 64>(p, stream) : launch_g<true, 128>(p, stream);
+  return p.D == 64 ? launch_g<false, 64>(p, stream) : launch_g<false, 128>(p, stream);
+}
+
+hipError_t launch_decode_merge(const float* part_o, const float* part_lse, int B, int Hq, int D, int S, float* out,
+                               float* lse, hipStream_t stream) {
+  dim3 grid(B * Hq);
+  if (D == 64)
+    decode_merge_kernel<64><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
+  else
+    decode_merge_kernel<128><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

@@ -1,0 +1,339 @@
+// C ABI of the cross-layer KV-sharing hot path: argument checks, launch
+// configuration and status codes. Nothing here allocates, frees or
+// synchronises; every check runs before anything is enqueued.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/yoco.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+yoco_status fail(yoco_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+yoco_status ok() {
+  g_err[0] = '\0';
+  return YOCO_OK;
+}
+
+size_t esize(yoco_dtype dt) { return dt == YOCO_BF16 ? 2 : 4; }
+
+bool valid_dtype(yoco_dtype dt) { return dt == YOCO_F32 || dt == YOCO_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte span [lo, hi) touched by rows [r0, r1) of a tensor with H heads, B batches.
+struct Span {
+  uintptr_t lo, hi;
+};
+
+Span span_of(const yoco_tensor4& t, int B, int H, int64_t r0, int64_t r1, int D, size_t es) {
+  // Strides are non-negative (checked), so the extremes are the first and last elements.
+  int64_t first = r0 * t.stride_t;
+  int64_t last = (int64_t)(B - 1) * t.stride_b + (int64_t)(H - 1) * t.stride_h + (r1 - 1) * t.stride_t + D;
+  uintptr_t base = reinterpret_cast<uintptr_t>(t.ptr);
+  return {base + (uintptr_t)(first * (int64_t)es), base + (uintptr_t)(last * (int64_t)es)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+yoco_status check_tensor(const char* name, const yoco_tensor4& t, int64_t rows_needed, size_t es) {
+  if (!t.ptr) return fail(YOCO_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (t.stride_b < 0 || t.stride_h < 0 || t.stride_t < 0)
+    return fail(YOCO_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (t.rows < rows_needed)
+    return fail(YOCO_ERR_INVALID_ARG, "%s: %lld rows, %lld needed", name, (long long)t.rows,
+                (long long)rows_needed);
+  if (!aligned16(t.ptr)) return fail(YOCO_ERR_ALIGNMENT, "%s: base pointer not 16-byte aligned", name);
+  if ((t.stride_b * (int64_t)es) % 16 || (t.stride_h * (int64_t)es) % 16 || (t.stride_t * (int64_t)es) % 16)
+    return fail(YOCO_ERR_ALIGNMENT, "%s: a stride is not a multiple of 16 bytes", name);
+  return YOCO_OK;
+}
+
+yoco::View4 view(const yoco_tensor4& t) { return {t.ptr, t.stride_b, t.stride_h, t.stride_t}; }
+
+yoco_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(YOCO_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+float fold(float lambda, float a) { return (float)((double)lambda * (double)a); }
+
+bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
+constexpr int kDecodeRowQuantum = 16;   // split lengths are multiples of this
+constexpr int kDecodeMinRows = 256;     // shortest automatic split
+constexpr int kDecodeTargetBlocks = 1024;
+
+int round_up(int64_t x, int64_t q) { return (int)(((x + q - 1) / q) * q); }
+
+int decode_rows_per_split(int T, int S) { return round_up((T + (int64_t)S - 1) / S, kDecodeRowQuantum); }
+
+yoco_status check_decode(const void* q, const yoco_tensor4& k, const yoco_tensor4& v, int B, int T, int Hq, int Hkv,
+                         int D, yoco_dtype dt) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0)
+    return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive (B=%d T=%d Hq=%d Hkv=%d D=%d)", B, T, Hq, Hkv, D);
+  if (Hq % Hkv) return fail(YOCO_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!valid_dtype(dt)) return fail(YOCO_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (D != 64 && D != 128) return fail(YOCO_ERR_UNSUPPORTED, "decode supports D in {64, 128}, got %d", D);
+  if (!supported_group(Hq / Hkv))
+    return fail(YOCO_ERR_UNSUPPORTED, "decode supports Hq/Hkv in {1,2,4,8,16}, got %d", Hq / Hkv);
+  if (!q) return fail(YOCO_ERR_INVALID_ARG, "q: null pointer");
+  if (!aligned16(q)) return fail(YOCO_ERR_ALIGNMENT, "q: not 16-byte aligned");
+  size_t es = esize(dt);
+  yoco_status st;
+  if ((st = check_tensor("k_cache", k, T, es)) != YOCO_OK) return st;
+  if ((st = check_tensor("v_cache", v, T, es)) != YOCO_OK) return st;
+  if ((int64_t)T * k.stride_t > (int64_t)INT32_MAX * 4 || (int64_t)T > INT32_MAX / 2)
+    return fail(YOCO_ERR_UNSUPPORTED, "cache too long");
+  return YOCO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* yoco_status_string(yoco_status s) {
+  switch (s) {
+    case YOCO_OK: return "ok";
+    case YOCO_ERR_INVALID_ARG: return "invalid argument";
+    case YOCO_ERR_UNSUPPORTED: return "unsupported";
+    case YOCO_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case YOCO_ERR_WORKSPACE: return "workspace missing or too small";
+    case YOCO_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* yoco_last_error(void) { return g_err; }
+
+int yoco_version(void) { return YOCO_VERSION; }
+
+yoco_status yoco_compose_kv(yoco_tensor4 k1, yoco_tensor4 ki, yoco_tensor4 v1, yoco_tensor4 vi, yoco_tensor4 k_cache,
+                            yoco_tensor4 v_cache, int t0, int B, int n, int Hkv, int D, float lambda, float aK1,
+                            float aK2, float aV1, float aV2, yoco_dtype dtype, hipStream_t stream) {
+  if (B <= 0 || n <= 0 || Hkv <= 0 || D <= 0 || t0 < 0)
+    return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive and t0 >= 0 (B=%d n=%d Hkv=%d D=%d t0=%d)", B, n, Hkv,
+                D, t0);
+  if (!valid_dtype(dtype)) return fail(YOCO_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  const size_t es = esize(dtype);
+  if ((D * es) % 16 || D > 1024)
+    return fail(YOCO_ERR_UNSUPPORTED, "compose needs D*elemsize a multiple of 16 bytes and D <= 1024 (D=%d)", D);
+  if (!isfinite(lambda) || !isfinite(aK1) || !isfinite(aK2) || !isfinite(aV1) || !isfinite(aV2))
+    return fail(YOCO_ERR_INVALID_ARG, "lambda and the weights must be finite");
+  if ((uint64_t)B * n * Hkv * (D * es / 16) >= (1ull << 31))
+    return fail(YOCO_ERR_UNSUPPORTED, "compose call too large (more than 2^31 16-byte vectors)");
+  yoco_status st;
+  const char* names[6] = {"k1", "ki", "v1", "vi", "k_cache", "v_cache"};
+  const yoco_tensor4* ts[6] = {&k1, &ki, &v1, &vi, &k_cache, &v_cache};
+  for (int i = 0; i < 6; ++i) {
+    int64_t need = i < 4 ? (int64_t)n : (int64_t)t0 + n;
+    if ((st = check_tensor(names[i], *ts[i], need, es)) != YOCO_OK) return st;
+  }
+  // Overlap rules: a source may alias a destination exactly (in-place, t0 = 0);
+  // any other overlap of a source with a destination is rejected, and so is
+  // k_cache overlapping v_cache with the same layout.
+  Span dst[2] = {span_of(k_cache, B, Hkv, t0, (int64_t)t0 + n, D, es),
+                 span_of(v_cache, B, Hkv, t0, (int64_t)t0 + n, D, es)};
+  for (int i = 0; i < 4; ++i) {
+    Span src = span_of(*ts[i], B, Hkv, 0, n, D, es);
+    for (int d = 0; d < 2; ++d) {
+      if (!overlap(src, dst[d])) continue;
+      const yoco_tensor4& a = *ts[i];
+      const yoco_tensor4& c = d == 0 ? k_cache : v_cache;
+      bool exact = a.ptr == c.ptr && a.stride_b == c.stride_b && a.stride_h == c.stride_h &&
+                   a.stride_t == c.stride_t && t0 == 0;
+      if (!exact)
+        return fail(YOCO_ERR_INVALID_ARG, "%s overlaps %s without aliasing it exactly", names[i], names[4 + d]);
+    }
+  }
+  if (k_cache.ptr == v_cache.ptr && k_cache.stride_b == v_cache.stride_b && k_cache.stride_h == v_cache.stride_h &&
+      k_cache.stride_t == v_cache.stride_t)
+    return fail(YOCO_ERR_INVALID_ARG, "k_cache and v_cache are the same buffer");
+
+  yoco::ComposeParams p;
+  p.k1 = view(k1);
+  p.ki = view(ki);
+  p.v1 = view(v1);
+  p.vi = view(vi);
+  p.kc = view(k_cache);
+  p.vc = view(v_cache);
+  p.t0 = t0;
+  p.B = B;
+  p.n = n;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.cK1 = fold(lambda, aK1);
+  p.cK2 = fold(lambda, aK2);
+  p.cV1 = fold(lambda, aV1);
+  p.cV2 = fold(lambda, aV2);
+  return launched(yoco::launch_compose(p, dtype == YOCO_BF16, stream), "compose");
+}
+
+int yoco_decode_num_splits(int B, int T, int Hq, int Hkv, int D) {
+  (void)Hq;
+  (void)D;
+  if (B <= 0 || T <= 0 || Hkv <= 0) return 0;
+  int64_t pairs = (int64_t)B * Hkv;
+  int64_t want = (kDecodeTargetBlocks + pairs - 1) / pairs;
+  int64_t most = std::max<int64_t>(1, T / kDecodeMinRows);
+  int S = (int)std::max<int64_t>(1, std::min(want, most));
+  // Drop splits that the rounding of the split length would leave empty.
+  int rps = decode_rows_per_split(T, S);
+  return (int)((T + (int64_t)rps - 1) / rps);
+}
+
+size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_splits) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_splits < 0) return 0;
+  int S = num_splits ? num_splits : yoco_decode_num_splits(B, T, Hq, Hkv, D);
+  if (S <= 1) return 0;
+  size_t rows = (size_t)B * Hq * S;
+  size_t o_bytes = rows * D * sizeof(float);
+  return o_bytes + round_up((int64_t)(rows * sizeof(float)), 16);
+}
+
+static yoco_status decode_setup(const void* q, yoco_tensor4 k, yoco_tensor4 v, const int32_t* seq_lens, int B, int T,
+                                int Hq, int Hkv, int D, float scale, void* workspace, size_t ws_bytes, int S,
+                                yoco_dtype dt, yoco::DecodeParams* p) {
+  yoco_status st = check_decode(q, k, v, B, T, Hq, Hkv, D, dt);
+  if (st != YOCO_OK) return st;
+  if (S < 1) return fail(YOCO_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", S);
+  if (S > T) return fail(YOCO_ERR_INVALID_ARG, "num_splits=%d exceeds T=%d", S, T);
+  if (seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(YOCO_ERR_ALIGNMENT, "seq_lens: not 4-byte aligned");
+  if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)D);
+  if (!isfinite(scale)) return fail(YOCO_ERR_INVALID_ARG, "scale must be finite");
+  p->q = q;
+  p->k = view(k);
+  p->v = view(v);
+  p->seq_lens = seq_lens;
+  p->B = B;
+  p->T = T;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->D = D;
+  p->scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p->num_splits = S;
+  p->rows_per_split = decode_rows_per_split(T, S);
+  p->out = nullptr;
+  p->lse = nullptr;
+  p->part_o = nullptr;
+  p->part_lse = nullptr;
+  if (S > 1) {
+    size_t need = yoco_decode_workspace_size(B, T, Hq, Hkv, D, S);
+    if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (ws_bytes < need) return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    if (!aligned16(workspace)) return fail(YOCO_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+    p->part_o = static_cast<float*>(workspace);
+    p->part_lse = p->part_o + (size_t)B * Hq * S * D;
+  }
+  return YOCO_OK;
+}
+
+yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
+                                   const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D, float scale,
+                                   float* out, float* lse, void* workspace, size_t workspace_bytes, int num_splits,
+                                   yoco_dtype kv_dtype, hipStream_t stream) {
+  if (num_splits < 0) return fail(YOCO_ERR_INVALID_ARG, "num_splits must be >= 0");
+  int S = num_splits ? num_splits : yoco_decode_num_splits(B, T, Hq, Hkv, D);
+  if (S == 0) return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive");
+  yoco::DecodeParams p;
+  yoco_status st =
+      decode_setup(q, k_cache, v_cache, seq_lens, B, T, Hq, Hkv, D, scale, workspace, workspace_bytes, S, kv_dtype, &p);
+  if (st != YOCO_OK) return st;
+  if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
+  if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
+  p.out = out;
+  p.lse = lse;
+  hipError_t e = yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream);
+  if (e != hipSuccess || S == 1) return launched(e, "decode split pass");
+  return launched(yoco::launch_decode_merge(p.part_o, p.part_lse, B, Hq, D, S, out, lse, stream), "decode merge");
+}
+
+yoco_status yoco_cross_attn_decode_partial(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
+                                           const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D, float scale,
+                                           void* workspace, size_t workspace_bytes, int num_splits,
+                                           yoco_dtype kv_dtype, hipStream_t stream) {
+  if (num_splits < 2)
+    return fail(YOCO_ERR_INVALID_ARG, "the split pass alone needs num_splits >= 2 (got %d)", num_splits);
+  yoco::DecodeParams p;
+  yoco_status st = decode_setup(q, k_cache, v_cache, seq_lens, B, T, Hq, Hkv, D, scale, workspace, workspace_bytes,
+                                num_splits, kv_dtype, &p);
+  if (st != YOCO_OK) return st;
+  return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode split pass");
+}
+
+yoco_status yoco_decode_merge(const void* workspace, size_t workspace_bytes, int B, int Hq, int D, int num_splits,
+                              float* out, float* lse, hipStream_t stream) {
+  if (B <= 0 || Hq <= 0 || num_splits < 2)
+    return fail(YOCO_ERR_INVALID_ARG, "B, Hq must be positive and num_splits >= 2");
+  if (D != 64 && D != 128) return fail(YOCO_ERR_UNSUPPORTED, "merge supports D in {64, 128}, got %d", D);
+  size_t rows = (size_t)B * Hq * num_splits;
+  size_t need = rows * D * sizeof(float) + rows * sizeof(float);
+  if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < need) return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(YOCO_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
+  if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
+  const float* po = static_cast<const float*>(workspace);
+  const float* pl = po + rows * D;
+  return launched(yoco::launch_decode_merge(po, pl, B, Hq, D, num_splits, out, lse, stream), "decode merge");
+}
+
+yoco_status yoco_cross_attn_prefill(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache, int B, int C, int p0,
+                                    int Hq, int Hkv, int D, float scale, void* out, yoco_dtype out_dtype, float* lse,
+                                    yoco_dtype dtype, hipStream_t stream) {
+  if (B <= 0 || C <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || p0 < 0)
+    return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive and p0 >= 0 (B=%d C=%d Hq=%d Hkv=%d D=%d p0=%d)", B, C,
+                Hq, Hkv, D, p0);
+  if (Hq % Hkv) return fail(YOCO_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return fail(YOCO_ERR_INVALID_ARG, "unknown dtype");
+  if (dtype != YOCO_BF16) return fail(YOCO_ERR_UNSUPPORTED, "prefill runs on bf16 inputs only");
+  if (D != 128) return fail(YOCO_ERR_UNSUPPORTED, "prefill supports D = 128, got %d", D);
+  if (!supported_group(Hq / Hkv))
+    return fail(YOCO_ERR_UNSUPPORTED, "prefill supports Hq/Hkv in {1,2,4,8,16}, got %d", Hq / Hkv);
+  if (!q) return fail(YOCO_ERR_INVALID_ARG, "q: null pointer");
+  if (!aligned16(q)) return fail(YOCO_ERR_ALIGNMENT, "q: not 16-byte aligned");
+  if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
+  if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
+  yoco_status st;
+  int64_t need = (int64_t)p0 + C;
+  if ((st = check_tensor("k_cache", k_cache, need, 2)) != YOCO_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, need, 2)) != YOCO_OK) return st;
+  if (need > INT32_MAX / 2) return fail(YOCO_ERR_UNSUPPORTED, "cache too long");
+  if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)D);
+  if (!isfinite(scale)) return fail(YOCO_ERR_INVALID_ARG, "scale must be finite");
+  yoco::PrefillParams p;
+  p.q = q;
+  p.k = view(k_cache);
+  p.v = view(v_cache);
+  p.B = B;
+  p.C = C;
+  p.p0 = p0;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.out = out;
+  p.out_bf16 = out_dtype == YOCO_BF16;
+  p.lse = lse;
+  return launched(yoco::launch_prefill(p, stream), "prefill");
+}
+
+}  // extern "C"

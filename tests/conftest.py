@@ -17,3 +17,14 @@ def pytest_configure(config):
 def has_gpu():
     import torch
     return torch.cuda.is_available()
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name every GPU case (flushed) before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.skip("needs a GPU")
+        print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield

@@ -1,0 +1,172 @@
+"""Host-side tests of the C ABI: the library loads, exports every function that
+include/yoco.h declares, and rejects bad arguments before any launch (these
+calls never reach the GPU, so they run on a CPU-only host)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import cross_layer_shared_amd as Y
+from cross_layer_shared_amd.binding import Tensor4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "yoco.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, LAUNCH = range(6)
+F32, BF16 = 0, 1
+BASE = 0x7F0000000000          # fake, 16-byte aligned device addresses (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return Y.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(yoco_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("yoco_compose_kv", "yoco_cross_attn_decode", "yoco_cross_attn_prefill", "yoco_decode_merge",
+              "yoco_cross_attn_decode_partial", "yoco_decode_workspace_size", "yoco_decode_num_splits"):
+        assert n in names
+    assert set(names) == set(Y.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", Y.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (yoco_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert Y.yoco_version() == 100
+    assert Y.yoco_status_string(OK) == "ok"
+    assert "workspace" in Y.yoco_status_string(WORKSPACE)
+    assert Y.yoco_status_string(99) == "unknown status"
+
+
+def t4(addr=BASE, sb=8 * 256 * 128, sh=256 * 128, st=128, rows=256):
+    return Tensor4(addr, sb, sh, st, rows)
+
+
+def src4(addr, n=256, Hkv=8, D=128, B=1):
+    # token-major [B, n, Hkv, D]
+    return Tensor4(addr, n * Hkv * D, D, Hkv * D, n)
+
+
+def compose(lib, **kw):
+    a = dict(k1=src4(BASE), ki=src4(BASE + (1 << 24)), v1=src4(BASE + (2 << 24)), vi=src4(BASE + (3 << 24)),
+             kc=t4(BASE + (4 << 24)), vc=t4(BASE + (5 << 24)), t0=0, B=1, n=256, Hkv=8, D=128, lam=35.0,
+             a=(0.01, 0.02, 0.03, 0.04), dt=BF16)
+    a.update(kw)
+    return lib.yoco_compose_kv(a["k1"], a["ki"], a["v1"], a["vi"], a["kc"], a["vc"], a["t0"], a["B"], a["n"],
+                               a["Hkv"], a["D"], a["lam"], *a["a"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(n=0), INVALID), (dict(t0=-1), INVALID), (dict(dt=7), INVALID),
+    (dict(D=60), UNSUPPORTED), (dict(D=2048), UNSUPPORTED),
+    (dict(k1=src4(0)), INVALID), (dict(kc=t4(0)), INVALID),
+    (dict(ki=src4(BASE + 8)), ALIGN), (dict(vc=t4(st=132)), ALIGN),
+    (dict(kc=t4(BASE + (4 << 24), rows=100)), INVALID), (dict(t0=1), INVALID),
+    (dict(lam=float("inf")), INVALID), (dict(a=(0.0, float("nan"), 0.0, 0.0)), INVALID),
+    # a source overlapping a destination without aliasing it exactly
+    (dict(ki=src4(BASE + (4 << 24) + 4096)), INVALID),
+    # the same source buffer as the cache but at t0 > 0 is a partial overlap
+    (dict(ki=t4(BASE + (4 << 24)), kc=t4(BASE + (4 << 24), rows=300), t0=16), INVALID),
+    (dict(vc=t4(BASE + (4 << 24))), INVALID),
+])
+def test_compose_rejects(lib, kw, status):
+    assert compose(lib, **kw) == status
+    assert Y.yoco_last_error() != ""
+
+
+def decode(lib, **kw):
+    a = dict(q=BASE, k=t4(BASE + (1 << 28), rows=4096, sb=8 * 4096 * 128, sh=4096 * 128),
+             v=t4(BASE + (2 << 28), rows=4096, sb=8 * 4096 * 128, sh=4096 * 128), sl=None, B=8, T=4096, Hq=32,
+             Hkv=8, D=128, scale=0.0, out=BASE + (3 << 28), lse=None, ws=BASE + (4 << 28), wsb=1 << 30, S=0,
+             dt=BF16)
+    a.update(kw)
+    return lib.yoco_cross_attn_decode(a["q"], a["k"], a["v"], a["sl"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                      a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], a["S"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(Hq=30), INVALID), (dict(dt=3), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(Hq=256), UNSUPPORTED), (dict(q=None), INVALID), (dict(q=BASE + 4), ALIGN),
+    (dict(out=None), INVALID), (dict(out=BASE + (3 << 28) + 8), ALIGN), (dict(lse=BASE + 2), ALIGN),
+    (dict(T=5000), INVALID), (dict(S=-1), INVALID), (dict(S=5000), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=1000), WORKSPACE), (dict(ws=BASE + 8), ALIGN),
+    (dict(sl=BASE + 2), ALIGN), (dict(scale=float("inf")), INVALID),
+])
+def test_decode_rejects(lib, kw, status):
+    assert decode(lib, **kw) == status
+    assert Y.yoco_last_error() != ""
+
+
+def test_partial_and_merge_reject(lib):
+    k = t4(BASE + (1 << 28), rows=4096)
+    assert lib.yoco_cross_attn_decode_partial(BASE, k, k, None, 1, 4096, 4, 1, 128, 0.0, BASE, 1 << 30, 1, BF16,
+                                              None) == INVALID
+    assert lib.yoco_decode_merge(BASE, 1 << 30, 1, 4, 96, 4, BASE, None, None) == UNSUPPORTED
+    assert lib.yoco_decode_merge(BASE, 100, 1, 4, 128, 4, BASE, None, None) == WORKSPACE
+    assert lib.yoco_decode_merge(BASE, 1 << 30, 1, 4, 128, 1, BASE, None, None) == INVALID
+    assert lib.yoco_decode_merge(None, 1 << 30, 1, 4, 128, 4, BASE, None, None) == WORKSPACE
+
+
+def prefill(lib, **kw):
+    a = dict(q=BASE, k=t4(BASE + (1 << 28), rows=8192, sb=8 * 8192 * 128, sh=8192 * 128),
+             v=t4(BASE + (2 << 28), rows=8192, sb=8 * 8192 * 128, sh=8192 * 128), B=1, C=4096, p0=4096, Hq=32,
+             Hkv=8, D=128, scale=0.0, out=BASE + (3 << 28), odt=F32, lse=None, dt=BF16)
+    a.update(kw)
+    return lib.yoco_cross_attn_prefill(a["q"], a["k"], a["v"], a["B"], a["C"], a["p0"], a["Hq"], a["Hkv"], a["D"],
+                                       a["scale"], a["out"], a["odt"], a["lse"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=0), INVALID), (dict(p0=-1), INVALID), (dict(p0=4097), INVALID), (dict(Hq=33), INVALID),
+    (dict(dt=F32), UNSUPPORTED), (dict(D=64), UNSUPPORTED), (dict(Hq=8 * 32), UNSUPPORTED), (dict(odt=9), INVALID),
+    (dict(q=BASE + 2), ALIGN), (dict(out=None), INVALID), (dict(lse=BASE + 1), ALIGN),
+    (dict(k=t4(BASE + 8, rows=8192)), ALIGN),
+])
+def test_prefill_rejects(lib, kw, status):
+    assert prefill(lib, **kw) == status
+    assert Y.yoco_last_error() != ""
+
+
+def test_split_heuristic_and_workspace():
+    assert Y.yoco_decode_num_splits(8, 4096, 32, 8, 128) == 16
+    assert Y.yoco_decode_num_splits(4, 131072, 32, 8, 128) == 32
+    assert Y.yoco_decode_num_splits(1, 1 << 20, 16, 4, 128) == 256
+    assert Y.yoco_decode_num_splits(1, 256, 4, 1, 64) == 1
+    assert Y.yoco_decode_num_splits(0, 256, 4, 1, 64) == 0
+    # [B, Hq, S, D] + [B, Hq, S] fp32
+    assert Y.yoco_decode_workspace_size(8, 4096, 32, 8, 128, 16) == 8 * 32 * 16 * 129 * 4
+    assert Y.yoco_decode_workspace_size(1, 256, 4, 1, 64, 1) == 0
+    for B, T, Hq, Hkv in [(3, 5, 4, 1), (1, 4097, 8, 2), (2, 100000, 16, 4)]:
+        s = Y.yoco_decode_num_splits(B, T, Hq, Hkv, 128)
+        assert 1 <= s <= T
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from cross_layer_shared_amd import binding
+    with pytest.raises(RuntimeError):
+        binding.load_library.__wrapped__(str(tmp_path / "missing.so")) if hasattr(binding.load_library, "__wrapped__") \
+            else _load_missing(binding, str(tmp_path / "missing.so"))
+
+
+def _load_missing(binding, path):
+    saved = binding._lib
+    binding._lib = None
+    try:
+        binding.load_library(path)
+    finally:
+        binding._lib = saved

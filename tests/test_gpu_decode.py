@@ -1,0 +1,234 @@
+"""GPU parity of the split-K decode (yoco_cross_attn_decode, its split pass and
+merge) against the fp64 oracle.
+
+Bar: fp32 caches within 1e-5 (per (b, h) row: ||o - o_ref||_inf <= 1e-5 ||o_ref||_inf);
+bf16 caches with fp32 accumulation within 1e-2 absolute; lse within the same
+bars. The scale-normalised error ||o - o_ref||_inf / rms(o_ref) is printed."""
+import numpy as np
+import pytest
+import torch
+
+import cross_layer_shared_amd as Y
+import oracle as O
+from synthetic import inputs as S
+from tests.gpu_util import dev, host, rowwise_rel, say
+
+pytestmark = pytest.mark.gpu
+
+BF16_ATOL = 1e-2
+F32_RTOL = 1e-5
+
+
+def _decode(q, k, v, splits=0, seq_lens=None, T=None):
+    B, Hq, D = q.shape
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    Y.yoco_cross_attn_decode(q, k, v, out, lse, seq_lens=sl, T=T, num_splits=splits)
+    torch.cuda.synchronize()
+    return host(out).astype(np.float64), host(lse).astype(np.float64)
+
+
+def _compare(o, lse, o_ref, lse_ref, dtype, mask=None):
+    if mask is not None:
+        o, lse, o_ref, lse_ref = o[mask], lse[mask], o_ref[mask], lse_ref[mask]
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    abs_err = np.max(np.abs(o - o_ref))
+    say(f"  max|o-ref| {abs_err:.3e}  /rms {abs_err / rms:.3e}  row-rel {rowwise_rel(o, o_ref):.3e}  "
+        f"max|lse-ref| {np.max(np.abs(lse - lse_ref)):.3e}")
+    if dtype == "f32":
+        assert rowwise_rel(o, o_ref) <= F32_RTOL
+        assert np.max(np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))) <= F32_RTOL
+    else:
+        assert abs_err <= BF16_ATOL
+        assert np.max(np.abs(lse - lse_ref)) <= BF16_ATOL
+
+
+def _inputs(B, T, Hq, Hkv, D, dtype, seed, q_std=1.0):
+    w = S.Workload("case", seed, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype)
+    k, v = S.cache_kv(w)
+    q = S.queries(w, std=q_std)
+    return q, k, v
+
+
+# ------------------------------------------------------------- tiny fp32 stack
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+def test_tiny_fp32_stack_end_to_end(splits):
+    """Compose layer 2 of a 4-layer stack, then one decode query per cross layer
+    (layers 3 and 4) over the shared K'_2, V'_2."""
+    w = S.TINY_FP32_STACK
+    src = S.compose_sources(w, layer=2)
+    alpha = S.alphas(w.seed, 2)
+    kc = torch.zeros((1, 1, w.T, w.D), dtype=torch.float32, device="cuda")
+    vc = torch.zeros_like(kc)
+    d = {k: dev(x) for k, x in src.items()}
+    Y.yoco_compose_kv(d["k1"], d["ki"], d["v1"], d["vi"], kc, vc, 0, alpha)
+    k_ref, v_ref = O.compose_kv(src["k1"], src["ki"], src["v1"], src["vi"], alpha)
+    k_ref, v_ref = k_ref.transpose(0, 2, 1, 3), v_ref.transpose(0, 2, 1, 3)   # -> [B, Hkv, T, D]
+    # The oracle attends over the exact composed cache; the GPU over its fp32
+    # rounding, which moves the result by far less than the 1e-5 bar.
+    for layer in (3, 4):
+        q = S.queries(w, layer=layer)
+        o, lse = _decode(dev(q), kc, vc, splits)
+        o_ref, lse_ref = O.decode_attention(q, k_ref, v_ref)
+        _compare(o, lse, o_ref, lse_ref, "f32")
+
+
+def test_yoco_plus_plus_at_init_equals_yoco():
+    """Decode over compose(identity init) equals decode over the raw K_i, V_i bit for bit."""
+    w = S.TINY_FP32_STACK
+    src = S.compose_sources(w, layer=2)
+    kc = torch.zeros((1, 1, w.T, w.D), dtype=torch.float32, device="cuda")
+    vc = torch.zeros_like(kc)
+    d = {k: dev(x) for k, x in src.items()}
+    Y.yoco_compose_kv(d["k1"], d["ki"], d["v1"], d["vi"], kc, vc, 0, S.IDENTITY_ALPHA)
+    raw_k = d["ki"].transpose(1, 2).contiguous()
+    raw_v = d["vi"].transpose(1, 2).contiguous()
+    q = dev(S.queries(w, layer=3))
+    o1, l1 = _decode(q, kc, vc)
+    o2, l2 = _decode(q, raw_k, raw_v)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------- shapes, tails, splits
+
+@pytest.mark.parametrize("T", [1, 63, 65, 1000, 4097])
+@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+def test_bf16_tails_and_splits(T, splits):
+    if splits > T:
+        pytest.skip("more splits than rows")
+    q, k, v = _inputs(2, T, 8, 2, 128, "bf16", 20 + T)
+    o, lse = _decode(dev(q), dev(k), dev(v), splits)
+    o_ref, lse_ref = O.decode_attention(q, k, v)
+    _compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "bf16"), (64, "f32"), (128, "f32")])
+def test_group_sizes_and_head_dims(G, D, dtype):
+    Hkv = 2
+    q, k, v = _inputs(2, 777, G * Hkv, Hkv, D, dtype, 30 + G + D)
+    o, lse = _decode(dev(q), dev(k), dev(v), 3)
+    o_ref, lse_ref = O.decode_attention(q, k, v)
+    _compare(o, lse, o_ref, lse_ref, dtype)
+
+
+@pytest.mark.parametrize("splits", [1, 5, 0])
+def test_ragged_seq_lens(splits):
+    """Per-sequence lengths (clamped to [1, T] on the device); rows past a length never matter."""
+    B, T = 5, 1500
+    q, k, v = _inputs(B, T, 8, 2, 128, "bf16", 40)
+    lens = [1500, 1, 700, 1499, 2000]           # the last is clamped to T
+    o, lse = _decode(dev(q), dev(k), dev(v), splits, seq_lens=lens)
+    o_ref, lse_ref = O.decode_attention(q, k, v, seq_lens=np.minimum(lens, T))
+    _compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    q, k, v = _inputs(2, 300, 8, 2, 128, "bf16", 41)
+    o1, l1 = _decode(dev(q), dev(k), dev(v), 4)
+    k4, v4 = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    o2, l2 = _decode(dev(q), dev(k4), dev(v4), 4)
+    assert np.max(np.abs(o1 - o2)) <= 1e-6 and np.max(np.abs(l1 - l2)) <= 1e-6
+
+
+def test_row_permutation_invariance():
+    q, k, v = _inputs(1, 999, 4, 1, 128, "bf16", 42)
+    perm = np.random.default_rng(0).permutation(999)
+    o1, l1 = _decode(dev(q), dev(k), dev(v), 5)
+    o2, l2 = _decode(dev(q), dev(np.ascontiguousarray(k[:, :, perm])), dev(np.ascontiguousarray(v[:, :, perm])), 5)
+    assert np.max(np.abs(o1 - o2)) <= 1e-5 and np.max(np.abs(l1 - l2)) <= 1e-5
+
+
+def test_split_pass_and_merge_entry_points():
+    """The split pass alone writes per-split (o_s, lse_s) equal to the oracle over
+    each split's rows; the merge of those equals the full decode."""
+    B, T, Hq, Hkv, D, S_ = 2, 1000, 8, 2, 128, 4
+    q, k, v = _inputs(B, T, Hq, Hkv, D, "bf16", 43)
+    ws = Y.decode_workspace(B, T, Hq, Hkv, D, S_)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    Y.yoco_cross_attn_decode_partial(qd, kd, vd, ws, S_)
+    torch.cuda.synchronize()
+    rows = B * Hq * S_
+    part_o = host(ws[: rows * D]).reshape(B, Hq, S_, D)
+    part_l = host(ws[rows * D: rows * D + rows]).reshape(B, Hq, S_)
+    rps = 256                                    # ceil(1000/4) = 250 rounded up to 16
+    for s in range(S_):
+        t0, t1 = s * rps, min(T, (s + 1) * rps)
+        o_ref, l_ref = O.decode_attention(q, k[:, :, t0:t1], v[:, :, t0:t1])
+        _compare(part_o[:, :, s].astype(np.float64), part_l[:, :, s].astype(np.float64), o_ref, l_ref, "bf16")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    Y.yoco_decode_merge(ws, B, Hq, D, S_, out, lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = O.decode_attention(q, k, v)
+    _compare(host(out).astype(np.float64), host(lse).astype(np.float64), o_ref, l_ref, "bf16")
+
+
+def test_identical_keys_give_mean_value():
+    q, k, v = _inputs(1, 2048, 4, 1, 128, "bf16", 44)
+    k[:] = k[:, :, :1]
+    o, _ = _decode(dev(q), dev(k), dev(v))
+    mean = O.to_f64(v)[0, 0].mean(axis=0)
+    assert np.max(np.abs(o[0] - mean[None, :])) <= 1e-4
+
+
+# ------------------------------------------------------------- full-size workloads
+
+def test_decode_mid_context_full():
+    """B=8, T=4096, 32/8 heads, D=128: all 16 cross layers over the same cache, all heads checked."""
+    w = S.DECODE_MID
+    k, v = S.cache_kv(w)
+    kd, vd = dev(k), dev(v)
+    for layer in range(w.layers):
+        q = S.queries(w, layer=layer, std=w.notes["q_std"])
+        o, lse = _decode(dev(q), kd, vd)
+        o_ref, lse_ref = O.decode_attention(q, k, v)
+        say(f"  layer {layer}:")
+        _compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def _sampled_heads(B, Hq, n, seed):
+    r = np.random.default_rng(seed)
+    pairs = {(int(r.integers(B)), int(r.integers(Hq))) for _ in range(n)}
+    pairs |= {(0, 0), (B - 1, Hq - 1)}
+    return sorted(pairs)
+
+
+@pytest.mark.slow
+def test_decode_long_context_full():
+    """B=4, T=131072, 32/8 heads, 1% of key rows scaled x8 (peaked softmax); sampled heads."""
+    w = S.DECODE_LONG
+    k, v = S.cache_kv(w)
+    S.scale_key_rows_bf16(k, S.scaled_rows(w), w.notes["scale"])
+    q = S.queries(w)
+    o, lse = _decode(dev(q), dev(k), dev(v))
+    heads = _sampled_heads(w.B, w.Hq, 10, 3)
+    o_ref, lse_ref = O.decode_attention(q, k, v, heads=heads)
+    mask = np.zeros((w.B, w.Hq), bool)
+    for b, h in heads:
+        mask[b, h] = True
+    _compare(o, lse, o_ref, lse_ref, "bf16", mask=mask)
+
+
+@pytest.mark.slow
+def test_decode_million_token_planted_row():
+    """B=1, T=2^20, 16/4 heads: one key row = 4*q at a seeded position dominates its head."""
+    w = S.DECODE_MILLION
+    k, v = S.cache_kv(w)
+    q = S.queries(w)
+    t_star = S.planted_position(w)
+    S.plant_query_row_bf16(k, q, t_star, w.notes["plant_scale"])
+    o, lse = _decode(dev(q), dev(k), dev(v))
+    G = w.G
+    heads = [(0, g * G) for g in range(w.Hkv)] + [(0, 1), (0, w.Hq - 1)]
+    o_ref, lse_ref = O.decode_attention(q, k, v, heads=heads)
+    mask = np.zeros((w.B, w.Hq), bool)
+    for b, h in heads:
+        mask[b, h] = True
+    _compare(o, lse, o_ref, lse_ref, "bf16", mask=mask)
+    for g in range(w.Hkv):
+        planted = O.to_f64(v[0, g, t_star])
+        say(f"  head {g * G}: max|o - V[t*]| = {np.max(np.abs(o[0, g * G] - planted)):.3e}")
+        assert np.max(np.abs(o[0, g * G] - planted)) <= BF16_ATOL
