@@ -1,0 +1,319 @@
+"""Benchmark of the cross-layer KV-sharing hot path on one MI355X.
+
+Headline step (the mid-context decode workload: B=8, T=4096, 32 query / 8 KV
+heads, D=128, bf16, 16 cross-decoder layers on one shared cache): compose the
+new token's K', V' row into the cache (n=1), then run the 16 cross layers'
+decode attention (split pass + log-sum-exp merge) over that same cache.
+``value`` is the algorithmic KV bytes the 16 decode calls must read (K' + V'
+once per layer) per second of step time.
+
+Further legs, reported in the same JSON line: the compose of the 32K-token
+prefill workload's 15 composed self-decoder layers (GB/s), the causal chunked
+prefill over that workload's global cache (TFLOP/s over unmasked pairs), the
+two long-context decodes (131K tokens x 4 sequences; 1M tokens), cold-cache
+decode timings, and a plain device copy as the achievable-bandwidth reference.
+
+cpu_baseline: the fp64 oracle (as it stands) timed on the host cores over a
+bounded sample of the headline workload (a few of its decode layers).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "decode-attn KV GB/s (% HBM peak), prefill TFLOP/s (% bf16 MFMA), compose GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
+    return ap.parse_args()
+
+
+def up(x, torch):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+class Flusher:
+    """Writes 1 GiB so that the 256 MB Infinity Cache holds none of the next kernel's inputs."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def timed(torch, fn, reps, flush=None):
+    """Average duration (ms) of fn() over reps launches, HIP events on the current stream."""
+    durs = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        durs.append(a.elapsed_time(b))
+    return float(np.mean(durs)), float(np.min(durs))
+
+
+# ----------------------------------------------------------------- headline
+
+def headline(args, torch, Y, S):
+    w = S.DECODE_MID
+    B, T, Hq, Hkv, D, L = w.B, w.T, w.Hq, w.Hkv, w.D, w.layers
+    k_bits, v_bits = S.cache_kv(w)
+    kc, vc = up(k_bits, torch), up(v_bits, torch)
+    qs = [up(S.queries(w, layer=l, std=w.notes["q_std"]), torch) for l in range(L)]
+    src = {k: up(v, torch) for k, v in S.compose_sources(w, layer=L // 2, n=1).items()}   # new token, layer L/2
+    alpha = S.alphas(w.seed, L // 2)
+    nsplit = Y.yoco_decode_num_splits(B, T, Hq, Hkv, D)
+    ws = Y.decode_workspace(B, T, Hq, Hkv, D, nsplit)
+    out = torch.empty((L, B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, B, Hq), dtype=torch.float32, device="cuda")
+    # one event pair per split-pass launch of the timed region, read after it ends
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+          for _ in range(args.steps)]
+
+    def step(marks):
+        Y.yoco_compose_kv(src["k1"], src["ki"], src["v1"], src["vi"], kc, vc, T - 1, alpha)
+        for l in range(L):
+            if marks is not None:
+                marks[l][0].record()
+            Y.yoco_cross_attn_decode_partial(qs[l], kc, vc, ws, nsplit)
+            if marks is not None:
+                marks[l][1].record()
+            Y.yoco_decode_merge(ws, B, Hq, D, nsplit, out[l], lse[l])
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record()
+    for i in range(args.steps):
+        step(ev[i])
+    e_ev.record()
+    torch.cuda.synchronize()
+    ms_per_step = s_ev.elapsed_time(e_ev) / args.steps
+    host_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    split_ms = [a.elapsed_time(b) for marks in ev for a, b in marks]
+
+    layer_bytes = 2 * B * T * Hkv * D * 2
+    value = L * layer_bytes / (ms_per_step * 1e-3) / 1e9
+    split_avg = float(np.mean(split_ms))
+    achieved = layer_bytes / (split_avg * 1e-3) / 1e9
+
+    # cold: Infinity Cache flushed before every split pass (the %-of-HBM figure)
+    flush = Flusher(torch)
+    cold_ms, cold_min = timed(torch, lambda: Y.yoco_cross_attn_decode_partial(qs[0], kc, vc, ws, nsplit), args.reps,
+                              flush)
+    merge_ms, _ = timed(torch, lambda: Y.yoco_decode_merge(ws, B, Hq, D, nsplit, out[0], lse[0]), args.reps)
+    del flush
+    return {
+        "value": value, "ms_per_step": ms_per_step, "host_ms_per_step": host_ms, "num_splits": nsplit,
+        "split_pass_avg_ms": split_avg, "split_pass_warm_gbs": achieved, "layer_bytes": layer_bytes,
+        "split_pass_cold_ms": cold_ms, "split_pass_cold_gbs": layer_bytes / (cold_ms * 1e-3) / 1e9,
+        "split_pass_cold_best_gbs": layer_bytes / (cold_min * 1e-3) / 1e9, "merge_ms": merge_ms,
+    }
+
+
+# ----------------------------------------------------------------- legs
+
+def leg_compose(args, torch, Y, S):
+    """Compose of the 15 composed self-decoder layers (i = 2..16) of the 32K-token workload."""
+    w = S.PREFILL_CHUNKED
+    B, T, Hkv, D = w.B, w.T, w.Hkv, w.D
+    k1 = up(S.layer_source(w, "k", 1), torch)
+    v1 = up(S.layer_source(w, "v", 1), torch)
+    layers = list(range(2, w.self_layers + 1))
+    res = []
+    flush = Flusher(torch)
+    kc = torch.empty((B, Hkv, T, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    bytes_per_call = 6 * B * T * Hkv * D * 2
+    for i in layers:
+        ki = up(S.layer_source(w, "k", i), torch)
+        vi = up(S.layer_source(w, "v", i), torch)
+        alpha = S.alphas(w.seed, i)
+        fn = lambda: Y.yoco_compose_kv(k1, ki, v1, vi, kc, vc, 0, alpha)  # noqa: E731
+        fn()
+        cold, cold_min = timed(torch, fn, max(2, args.reps // 3), flush)
+        warm, _ = timed(torch, fn, max(2, args.reps // 3))
+        res.append((cold, cold_min, warm))
+        del ki, vi
+    del flush
+    cold = float(np.mean([r[0] for r in res]))
+    best = float(np.min([r[1] for r in res]))
+    warm = float(np.mean([r[2] for r in res]))
+    return {"workload": "prefill_chunked stage A (15 compose calls, [1,32768,8,128] bf16)",
+            "bytes_per_call": bytes_per_call, "cold_ms": cold, "cold_gbs": bytes_per_call / cold / 1e6,
+            "cold_best_gbs": bytes_per_call / best / 1e6, "back_to_back_ms": warm,
+            "back_to_back_gbs": bytes_per_call / warm / 1e6,
+            "hbm_frac_cold": bytes_per_call / cold / 1e6 / HBM_PEAK_GBS}
+
+
+def leg_prefill(args, torch, Y, S):
+    w = S.PREFILL_CHUNKED
+    B, T, Hq, Hkv, D, C = w.B, w.T, w.Hq, w.Hkv, w.D, w.chunk
+    k_bits, v_bits = S.cache_kv(w)
+    kc, vc = up(k_bits, torch), up(v_bits, torch)
+    q = up(S.queries(w, rows=T), torch)
+    out = torch.empty((B, T, Hq, D), dtype=torch.float32, device="cuda")
+
+    def run():
+        for c0 in range(0, T, C):
+            Y.yoco_cross_attn_prefill(q[:, c0:c0 + C], kc, vc, c0, out[:, c0:c0 + C])
+
+    run()
+    torch.cuda.synchronize()
+    ms, best = timed(torch, run, max(2, args.reps // 2))
+    flop = 4.0 * B * Hq * D * T * (T + 1) / 2
+    return {"workload": "prefill_chunked (T=32768, chunk 4096, 32/8 heads, D=128, bf16)", "flop": flop,
+            "ms": ms, "tflops": flop / ms / 1e9, "best_tflops": flop / best / 1e9,
+            "mfma_frac": flop / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS}
+
+
+def leg_long_decode(args, torch, Y, S, w, planted=False):
+    k_bits, v_bits = S.cache_kv(w)
+    q_bits = S.queries(w)
+    if planted:
+        S.plant_query_row_bf16(k_bits, q_bits, S.planted_position(w), w.notes["plant_scale"])
+    else:
+        S.scale_key_rows_bf16(k_bits, S.scaled_rows(w), w.notes["scale"])
+    kc, vc = up(k_bits, torch), up(v_bits, torch)
+    del k_bits, v_bits
+    q = up(q_bits, torch)
+    B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
+    nsplit = Y.yoco_decode_num_splits(B, T, Hq, Hkv, D)
+    ws = Y.decode_workspace(B, T, Hq, Hkv, D, nsplit)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    flush = Flusher(torch)
+    full = lambda: Y.yoco_cross_attn_decode(q, kc, vc, out, workspace=ws, num_splits=nsplit)  # noqa: E731
+    part = lambda: Y.yoco_cross_attn_decode_partial(q, kc, vc, ws, nsplit)  # noqa: E731
+    full()
+    ms, best = timed(torch, full, args.reps, flush)
+    pms, _ = timed(torch, part, args.reps, flush)
+    nbytes = 2 * B * T * Hkv * D * 2
+    return {"workload": w.name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "num_splits": nsplit, "bytes": nbytes,
+            "ms": ms, "gbs": nbytes / ms / 1e6, "best_gbs": nbytes / best / 1e6, "split_pass_ms": pms,
+            "split_pass_gbs": nbytes / pms / 1e6, "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+
+
+def leg_copy(args, torch):
+    """A plain device-to-device copy of 1 GiB: the achievable-bandwidth reference."""
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    flush = Flusher(torch)
+    ms, best = timed(torch, lambda: dst.copy_(src), args.reps, flush)
+    nbytes = 2 * src.numel() * 2
+    return {"bytes": nbytes, "ms": ms, "gbs": nbytes / ms / 1e6, "best_gbs": nbytes / best / 1e6}
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(args, S):
+    """The fp64 oracle on the host: decode layers of the headline workload until
+    about --cpu-seconds of work; reported in the headline unit (GB/s of KV)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    w = S.DECODE_MID
+    k_bits, v_bits = S.cache_kv(w)
+    layer_bytes = 2 * w.B * w.T * w.Hkv * w.D * 2
+    layers, t_total = 0, 0.0
+    while t_total < args.cpu_seconds and layers < w.layers:
+        q = S.queries(w, layer=layers, std=w.notes["q_std"])
+        t0 = time.perf_counter()
+        O.decode_attention(q, k_bits, v_bits)
+        t_total += time.perf_counter() - t0
+        layers += 1
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"value": layers * layer_bytes / t_total / 1e9, "unit": "GB/s", "cores": threads or cores,
+            "host_cores_available": cores, "kind": "oracle",
+            "sample": f"{layers} of the 16 decode layers of decode_mid_context (fp64 NumPy, {t_total:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+                                   "(the hot path has no multi-GPU mode)"}))
+        sys.exit(2)
+    import torch
+
+    import cross_layer_shared_amd as Y
+    from synthetic import inputs as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    Y.load_library()
+    legs = {"compose", "prefill", "long", "million", "copy"} if args.legs == "all" else \
+        set() if args.legs == "headline" else set(args.legs.split(","))
+
+    h = headline(args, torch, Y, S)
+    extra = {}
+    if "copy" in legs:
+        extra["copy_reference"] = leg_copy(args, torch)
+    if "compose" in legs:
+        extra["compose"] = leg_compose(args, torch, Y, S)
+    if "prefill" in legs:
+        extra["prefill"] = leg_prefill(args, torch, Y, S)
+    if "long" in legs:
+        extra["decode_long_context"] = leg_long_decode(args, torch, Y, S, S.DECODE_LONG)
+    if "million" in legs:
+        extra["decode_million_token"] = leg_long_decode(args, torch, Y, S, S.DECODE_MILLION, planted=True)
+    torch.cuda.synchronize()
+
+    w = S.DECODE_MID
+    roofline = {"kernel": "decode_split_kernel<bf16, D=128, G=4>", "bound": "hbm",
+                "achieved": h["split_pass_warm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": h["split_pass_warm_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                "algorithmic_bytes_per_launch": h["layer_bytes"], "avg_launch_ms": h["split_pass_avg_ms"],
+                "note": "16 layers re-read one 128 MiB cache, which fits the 256 MB Infinity Cache; "
+                        "cold (flushed) figure: split_pass_cold_gbs"}
+    line = {
+        "metric": METRIC, "value": h["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "cross_layers": w.layers, "step": "compose 1 new row + 16 x (decode split pass + merge)"},
+        "roofline": roofline,
+        "headline_detail": h,
+        "legs": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, S)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
