@@ -91,6 +91,12 @@ def _stream(stream) -> int | None:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _need_contiguous(**tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor")
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -151,6 +157,7 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T:
                            stream=None) -> None:
     """q [B, Hq, D]; caches [B, Hkv, T, D]; out [B, Hq, D] fp32; lse [B, Hq] fp32."""
     lib = load_library()
+    _need_contiguous(q=q, out=out, lse=lse, seq_lens=seq_lens)
     B, Hq, D = q.shape
     kc, vc = _as_t4(k_cache), _as_t4(v_cache)
     Hkv = k_cache.shape[1] if isinstance(k_cache, torch.Tensor) else None
@@ -166,6 +173,7 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T:
 def yoco_cross_attn_decode_partial(q, k_cache, v_cache, workspace, num_splits: int, seq_lens=None,
                                    T: int | None = None, scale: float = 0.0, stream=None) -> None:
     lib = load_library()
+    _need_contiguous(q=q, workspace=workspace, seq_lens=seq_lens)
     B, Hq, D = q.shape
     kc, vc = _as_t4(k_cache), _as_t4(v_cache)
     Hkv = k_cache.shape[1]
@@ -177,6 +185,7 @@ def yoco_cross_attn_decode_partial(q, k_cache, v_cache, workspace, num_splits: i
 
 def yoco_decode_merge(workspace, B: int, Hq: int, D: int, num_splits: int, out, lse=None, stream=None) -> None:
     lib = load_library()
+    _need_contiguous(workspace=workspace, out=out, lse=lse)
     _check(lib.yoco_decode_merge(workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, Hq, D,
                                  int(num_splits), out.data_ptr(), _ptr(lse), _stream(stream)))
 
@@ -185,6 +194,9 @@ def yoco_cross_attn_prefill(q, k_cache, v_cache, p0: int, out, lse=None, scale: 
     """q [B, C, Hq, D] bf16; caches [B, Hkv, Tcap, D] bf16; out [B, C, Hq, D] fp32 or bf16; lse [B, Hq, C]."""
     lib = load_library()
     B, C, Hq, D = q.shape
+    # a chunk sliced out of a [B, T, Hq, D] tensor is row-contiguous per sequence
+    # but not across sequences when B > 1; the kernel needs [B, C, Hq, D] dense
+    _need_contiguous(q=q, out=out, lse=lse)
     kc, vc = _as_t4(k_cache), _as_t4(v_cache)
     Hkv = k_cache.shape[1]
     _check(lib.yoco_cross_attn_prefill(q.data_ptr(), kc, vc, B, C, int(p0), Hq, Hkv, D, float(scale), out.data_ptr(),
