@@ -5,9 +5,11 @@
 //
 // Dense contraction on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 // A workgroup of 4 wavefronts serves 4 (head, 32-query block) slots that share
-// one kv head; it streams the cache in 64-key tiles staged through LDS, K
-// row-major and V transposed, so that all four wavefronts read each tile
-// from LDS instead of from memory.
+// one kv head; it streams the cache in 64-key tiles staged through LDS (two
+// stages, one barrier per tile), so that all four wavefronts read each tile
+// from LDS instead of from memory. K and V are both stored row-major; the V
+// operand of the PV product is read with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16), which hands each lane 4 consecutive keys of one dim.
 //
 // Per wavefront and tile:
 //   S^T = K Q^T   (2 x 32 keys by 32 queries; D = 128 in 8 MFMA k-steps)
@@ -18,7 +20,7 @@
 // become the P^T operand of the PV product without leaving the lane: the key
 // rows of each 32-key block are fed to the MFMA in the order that swaps bits 2
 // and 3 of the key index, which makes the 8 P values a lane holds for one PV
-// k-step 8 consecutive keys, i.e. one 16-byte read of the transposed V tile.
+// k-step 8 consecutive keys: two transposing reads of 4 keys each.
 // Probabilities are rounded to bf16 for the PV product; the normaliser sums
 // the same fp32 values.
 
@@ -34,14 +36,24 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 32;               // queries per wavefront
 constexpr int kKT = 64;               // keys per tile
-constexpr int kKPad = kD + 8;         // K tile row stride (bf16 elements)
-constexpr int kVPad = kKT + 8;        // transposed V tile row stride (bf16 elements)
+constexpr int kKPad = kD + 8;         // K tile row stride (bf16): 68 dwords, 16-lane b128 reads hit distinct banks
+constexpr int kVPad = kD + 16;        // V tile row stride (bf16): 72 dwords, 4-row tr reads hit distinct banks
+constexpr int kStage = kKT * kKPad + kKT * kVPad;   // bf16 elements per LDS stage
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte rows addressed by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ s16x4 read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<__bf16*>(p)));
+}
 
 // Row of a 32-key block that MFMA row i carries: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm_key(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -64,10 +76,9 @@ __device__ __forceinline__ float xor32_sum(float x) {
 }
 
 template <int HPW, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillParams p) {
   constexpr int WQ = kWaves / HPW;  // query blocks per workgroup
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kKT * kKPad];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kD * kVPad];
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -97,83 +108,95 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // cooperative tile loads: thread t covers dims 8*(t%16) .. +8 of keys 4*(t/16) .. +4
   const int ld_d = 8 * (tid & 15);
   const int ld_k = 4 * (tid >> 4);
+  const int64_t kst = p.k.st * 2, vst = p.v.st * 2;
   const char* kbase = static_cast<const char*>(p.k.ptr) + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh + ld_d) * 2;
   const char* vbase = static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh + ld_d) * 2;
-  const int64_t kst = p.k.st * 2, vst = p.v.st * 2;
   u32x4 kreg[4], vreg[4];
   auto load_tile = [&](int t) {
+    const int row0 = t * kKT + ld_k;
+    if (t * kKT + kKT <= kv_len) {          // whole tile inside the cache prefix: no clamping
+      const char* kp = kbase + row0 * kst;
+      const char* vp = vbase + row0 * vst;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + i * kst));
+        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * vst));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(row0 + i, kv_len - 1);
+        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + row * kst));
+        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + row * vst));
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    __bf16* kl = lds + stage * kStage;
+    __bf16* vl = kl + kKT * kKPad;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = min(t * kKT + ld_k + i, kv_len - 1);
-      kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + row * kst));
-      vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + row * vst));
+      *reinterpret_cast<u32x4*>(&kl[(ld_k + i) * kKPad + ld_d]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&vl[(ld_k + i) * kVPad + ld_d]) = vreg[i];
     }
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&k_lds[(ld_k + i) * kKPad + ld_d]) = kreg[i];
-    // transpose: for each of the 8 dims, the 4 keys ld_k..ld_k+3 as one 8-byte write
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][e], vreg[0][e], 0x05040100u);  // dim 2e:   k0 | k1
-      const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][e], vreg[2][e], 0x05040100u);  //          k2 | k3
-      const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][e], vreg[0][e], 0x07060302u);  // dim 2e+1
-      const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][e], vreg[2][e], 0x07060302u);
-      u32x2 lo = {lo01, lo23}, hi = {hi01, hi23};
-      *reinterpret_cast<u32x2*>(&vt_lds[(ld_d + 2 * e) * kVPad + ld_k]) = lo;
-      *reinterpret_cast<u32x2*>(&vt_lds[(ld_d + 2 * e + 1) * kVPad + ld_k]) = hi;
-    }
-  };
+
+  // Lane roles of the transposing V reads: group gq = lane/16, s = lane%16 addresses
+  // V[key + 8*(gq/2) + s/4][dim + 16*(gq%2) + 4*(s%4)] and receives dim (lane % 32)
+  // of 4 consecutive keys.
+  const int gq = lane >> 4, sl16 = lane & 15;
+  const int tr_off = (8 * (gq >> 1) + (sl16 >> 2)) * kVPad + 16 * (gq & 1) + 4 * (sl16 & 3);
+  const int k_off = perm_key(j) * kKPad + 8 * q;
 
   f32x16 o_acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;   // running max of scaled scores (log2 domain)
+  float l_run = 0.f;         // this lane's share of the running sum
   const float sl = p.scale_log2;
-  const int first_masked_tile = (p.p0 + c_wg) / kKT;  // tiles before it are fully visible to every query
 
-  load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
+  // One 64-key tile: scores, online softmax, PV, and the hand-over of the next tile.
+  auto tile = [&]<bool MASKED>(int t) {
+    const int stage = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
+    const __bf16* kl = lds + stage * kStage;
+    const __bf16* vl = kl + kKT * kKPad;
 
-    // ---- S^T = K Q^T for 2 blocks of 32 keys ----
-    f32x16 s[2];
+    // ---- S^T = K Q^T for 2 blocks of 32 keys (raw dot products) ----
+    f32x16 sc[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[hb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[hb][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[(32 * hb + perm_key(j)) * kKPad + 16 * c + 8 * q]);
-        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[hb], 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[32 * hb * kKPad + k_off + 16 * c]);
+        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[hb], 0, 0, 0);
       }
     }
 
-    // ---- mask, scale, tile max ----
-    const int key0 = t * kKT;
-    const bool masked = t >= first_masked_tile;
+    // ---- causal mask (diagonal tiles only), tile max ----
+    if constexpr (MASKED) {
+      const int key0 = t * kKT;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * hb + perm_key(8 * (r >> 2) + 4 * q + (r & 3));
+          if (key > pos) sc[hb][r] = -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[hb][r] * sl;
-        if (masked) {
-          const int key = key0 + 32 * hb + perm_key(8 * (r >> 2) + 4 * q + (r & 3));
-          if (key > pos) v = -INFINITY;
-        }
-        s[hb][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    }
-    mt = xor32_max(mt);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[hb][r]);
+    // the scale is positive, so the max of the scaled scores is the scaled max
+    mt = xor32_max(mt) * sl;
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
@@ -186,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
     m_run = m_new;
 
-    // ---- P = exp2(S - m), row sums, bf16 P^T operands ----
+    // ---- P = exp2(scale * S - m), row sums, bf16 P^T operands ----
     bf16x8 pb[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -195,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0v = fast_exp2(s[hb][8 * hs + 2 * e] - m_use);
-          const float p1v = fast_exp2(s[hb][8 * hs + 2 * e + 1] - m_use);
+          const float p0v = fast_exp2(__builtin_fmaf(sc[hb][8 * hs + 2 * e], sl, -m_use));
+          const float p1v = fast_exp2(__builtin_fmaf(sc[hb][8 * hs + 2 * e + 1], sl, -m_use));
           l_run += p0v + p1v;
           w[e] = pack2(p0v, p1v);
         }
@@ -210,15 +233,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
+        const __bf16* vk = vl + (32 * hb + 16 * hs) * kVPad + tr_off;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&vt_lds[(32 * db + j) * kVPad + 32 * hb + 16 * hs + 8 * q]);
-          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[hb][hs], o_acc[db], 0, 0, 0);
+          const s16x4 lo = read_tr16(vk + 32 * db);
+          const s16x4 hi = read_tr16(vk + 32 * db + 4 * kVPad);
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[hb][hs], o_acc[db],
+                                                              0, 0, 0);
         }
       }
     }
-  }
+
+    if (t + 1 < n_tiles) store_tile(stage ^ 1);
+    __syncthreads();
+  };
+
+  // Tiles before first_masked hold only keys <= every query position of the workgroup.
+  const int first_masked = min((p.p0 + c_wg) / kKT, n_tiles);
+  load_tile(0);
+  store_tile(0);
+  // Every load issued so far (Q and the first tile) is complete here, so the
+  // loop's waits only cover the tile prefetched inside it.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  for (int t = 0; t < first_masked; ++t) tile.template operator()<false>(t);
+  for (int t = first_masked; t < n_tiles; ++t) tile.template operator()<true>(t);
 
   // ---- normalise and write ----
   const float l_tot = xor32_sum(l_run);
