@@ -57,7 +57,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_cross_attn_decode.restype = st
     lib.yoco_cross_attn_decode_partial.argtypes = [vp, T4, T4, vp, i, i, i, i, i, f, vp, sz, i, i, vp]
     lib.yoco_cross_attn_decode_partial.restype = st
-    lib.yoco_decode_merge.argtypes = [vp, sz, i, i, i, i, vp, vp, vp]
+    lib.yoco_decode_merge.argtypes = [vp, sz, i, i, i, i, i, vp, vp, vp]
     lib.yoco_decode_merge.restype = st
     lib.yoco_cross_attn_prefill.argtypes = [vp, T4, T4, i, i, i, i, i, i, f, vp, i, vp, i, vp]
     lib.yoco_cross_attn_prefill.restype = st
@@ -148,8 +148,9 @@ def yoco_decode_workspace_size(B: int, T: int, Hq: int, Hkv: int, D: int, num_sp
 
 
 def decode_workspace(B, T, Hq, Hkv, D, num_splits=0, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (its counter section must start at zero)."""
     nbytes = max(16, yoco_decode_workspace_size(B, T, Hq, Hkv, D, num_splits))
-    return torch.empty(math.ceil(nbytes / 16) * 4, dtype=torch.float32, device=device)
+    return torch.zeros(math.ceil(nbytes / 16) * 4, dtype=torch.float32, device=device)
 
 
 def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T: int | None = None,
@@ -183,10 +184,11 @@ def yoco_cross_attn_decode_partial(q, k_cache, v_cache, workspace, num_splits: i
                                               int(num_splits), _dtype_code(q), _stream(stream)))
 
 
-def yoco_decode_merge(workspace, B: int, Hq: int, D: int, num_splits: int, out, lse=None, stream=None) -> None:
+def yoco_decode_merge(workspace, B: int, Hq: int, Hkv: int, D: int, num_splits: int, out, lse=None,
+                      stream=None) -> None:
     lib = load_library()
     _need_contiguous(workspace=workspace, out=out, lse=lse)
-    _check(lib.yoco_decode_merge(workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, Hq, D,
+    _check(lib.yoco_decode_merge(workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, Hq, Hkv, D,
                                  int(num_splits), out.data_ptr(), _ptr(lse), _stream(stream)))
 
 

@@ -31,10 +31,13 @@ struct DecodeParams {
   float scale_log2;       // softmax scale * log2(e)
   int num_splits;
   int rows_per_split;
+  int waves;              // wavefronts per workgroup: 4, 8 or 16
+  bool prefetch;          // double-buffered row loads (short splits)
   float* out;             // [B, Hq, D] (used when num_splits == 1)
   float* lse;             // [B, Hq] or null (used when num_splits == 1)
   float* part_o;          // [B, Hq, S, D]   (used when num_splits > 1)
   float* part_lse;        // [B, Hq, S]
+  unsigned* tickets;      // [B, Hkv] zero-initialised counters, or null (no fused merge)
 };
 hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode_merge(const float* part_o, const float* part_lse, int B, int Hq, int D, int S,

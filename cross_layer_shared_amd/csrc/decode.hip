@@ -23,8 +23,10 @@
 // rescales the value sums when some lane's maximum grew. The four groups and
 // four wavefronts merge their states once per split.
 //
-// Merge pass: the splits' normalised outputs are combined with their
-// log-sum-exps.
+// Merge: the splits' normalised outputs are combined with their log-sum-exps.
+// In the combined entry point the merge is fused: every workgroup takes a
+// ticket (atomic counter per (b, g)) after writing its partial, and the last
+// one merges the S partials of its G heads and resets the counter to zero.
 
 #include <math.h>
 
@@ -139,8 +141,63 @@ struct Unroll<N, N> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool BF16, int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+// Agent-scope relaxed atomic accesses: on gfx950 they are performed coherently
+// across the XCDs (write-through / read-through of the per-XCD L2), which is
+// what the fused merge needs without an L2-wide writeback per workgroup.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LSE merge of S split partials for G consecutive heads (rows bh0 .. bh0+G-1 of
+// [B*Hq]); the heads are spread over the NW wavefronts. Per head: M = max_s lse_s
+// (lanes stride over the splits), then the weighted sum over the splits in
+// batches of 8 whose loads are all issued before they are used.
+template <int D, int G, int NW, bool AGENT>
+__device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                             int S, int bh0, float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int PER = D / 64;
+  constexpr int BATCH = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto ld = [](const float* p) { return AGENT ? load_agent(p) : *p; };
+  for (int hh = wave; hh < G; hh += NW) {
+    const size_t r0 = (size_t)(bh0 + hh) * S;
+    float M = -INFINITY;
+    for (int i = lane; i < S; i += 64) M = fmaxf(M, ld(&part_lse[r0 + i]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f, o[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = 0.f;
+    for (int i0 = 0; i0 < S; i0 += BATCH) {
+      float li[BATCH], ov[BATCH][PER];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int i = min(i0 + u, S - 1);
+        li[u] = ld(&part_lse[r0 + i]);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) ov[u][k] = ld(&part_o[(r0 + i) * D + lane + 64 * k]);
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        // empty splits (lse = -inf) and the clamped tail of the last batch weigh 0
+        const float w = (i0 + u >= S || li[u] == -INFINITY) ? 0.f : __expf(li[u] - M);
+        L += w;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(w, ov[u][k], o[k]);
+      }
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) out[(size_t)(bh0 + hh) * D + lane + 64 * k] = o[k] * inv;
+    if (lse && lane == 0) lse[bh0 + hh] = M + logf(L);
+  }
+}
+
+template <bool BF16, int D, int G, int NW, bool PREFETCH>
+__global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   using L = Layout<BF16, D>;
   using vec = typename L::vec;
   constexpr int EPL = L::kEPL;
@@ -148,9 +205,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   constexpr int U = 16 / G;          // rows per group per iteration
   constexpr int R = 4 * U;           // rows per wavefront per iteration
 
-  __shared__ float sm_acc[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
+  __shared__ float sm_acc[NW][G][D];
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -189,8 +246,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                       s * EPL * L::kES;
   const int64_t kst = p.k.st * L::kES, vst = p.v.st * L::kES;
 
-  for (int base = ts + wave * R; base < te; base += kWaves * R) {
-    vec kr[U], vr[U];
+  auto load = [&](int base, vec (&kr)[U], vec (&vr)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int row = min(base + 4 * u + j, te - 1);
@@ -201,7 +257,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       int row = min(base + 4 * u + j, te - 1);
       vr[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(vbase + row * vst));
     }
+  };
 
+  auto rows = [&](const vec (&kr)[U], const vec (&vr)[U], int base) {
     // Partial dot products over this lane's slice: x[u*G + hh].
     float x[16];
 #pragma unroll
@@ -256,6 +314,37 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         }
       }
     });
+  };
+
+  // Rows of this wavefront: base, base + STEP, ... With PREFETCH the next
+  // block's loads are in flight while the current block is consumed (two
+  // register sets); short splits need that, long ones prefer the occupancy.
+  constexpr int STEP = NW * R;
+  int base = ts + wave * R;
+  if constexpr (PREFETCH) {
+    if (base < te) {
+      vec ka[U], va[U], kb[U], vb[U];
+      load(base, ka, va);
+      while (true) {
+        const int nb = base + STEP;
+        if (nb < te) load(nb, kb, vb);
+        rows(ka, va, base);
+        base = nb;
+        if (base >= te) break;
+        const int nb2 = base + STEP;
+        if (nb2 < te) load(nb2, ka, va);
+        rows(kb, vb, base);
+        base = nb2;
+        if (base >= te) break;
+      }
+    }
+  } else {
+    // one register set: fewer registers, more wavefronts resident per SIMD
+    for (; base < te; base += STEP) {
+      vec kr[U], vr[U];
+      load(base, kr, vr);
+      rows(kr, vr, base);
+    }
   }
 
   // ---- merge the four groups of the wavefront ----
@@ -293,14 +382,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 
   // ---- merge the wavefronts and write this split's result ----
   const int h0 = g * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
     const int hh = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][hh]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
     float Lsum = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       float m = sm_m[w][hh];
       float wt = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
       Lsum += wt * sm_l[w][hh];
@@ -315,87 +404,86 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       if (p.lse && d == 0) p.lse[(size_t)b * p.Hq + h] = lse;
     } else {
       const size_t row = ((size_t)b * p.Hq + h) * p.num_splits + split;
-      p.part_o[row * D + d] = o;
-      if (d == 0) p.part_lse[row] = lse;
+      if (p.tickets) {          // published to the merging workgroup, possibly on another XCD
+        store_agent(&p.part_o[row * D + d], o);
+        if (d == 0) store_agent(&p.part_lse[row], lse);
+      } else {
+        p.part_o[row * D + d] = o;
+        if (d == 0) p.part_lse[row] = lse;
+      }
     }
   }
+  if (p.num_splits == 1 || p.tickets == nullptr) return;
+
+  // ---- fused merge: the last workgroup of (b, g) to finish merges all splits ----
+  // Every wave drains its partial stores (acknowledged at agent scope) before
+  // the barrier, so the ticket is taken only after the whole partial is visible.
+  __shared__ int sm_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(&p.tickets[b * p.Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = old == (unsigned)(p.num_splits - 1);
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  merge_splits<D, G, NW, true>(p.part_o, p.part_lse, p.num_splits, b * p.Hq + h0, p.out, p.lse);
+  if (threadIdx.x == 0)   // ready for the next call
+    __hip_atomic_store(&p.tickets[b * p.Hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup (4 wavefronts) per (b, h): wavefront w takes splits w, w+4, ...;
-// lanes run over the head dimension.
-template <int D>
+// Standalone merge: one workgroup of 4 wavefronts per (b, group of 4 heads), one head per wavefront.
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __restrict__ part_o,
                                                                 const float* __restrict__ part_lse, int S,
                                                                 float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int PER = D / 64;
-  __shared__ float red[kWaves];
-  __shared__ float sm_o[kWaves][D];
-  __shared__ float sm_l[kWaves];
-  const int bh = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* pl = part_lse + (size_t)bh * S;
-  const float* po = part_o + (size_t)bh * S * D;
-
-  float M = -INFINITY;
-  for (int i = threadIdx.x; i < S; i += kThreads) M = fmaxf(M, pl[i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-  float o[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  float wsum = 0.f;
-#pragma unroll 4
-  for (int i = wave; i < S; i += kWaves) {
-    const float li = pl[i];
-    const float w = (li == -INFINITY) ? 0.f : __expf(li - M);
-    wsum += w;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(w, po[(size_t)i * D + lane + 64 * k], o[k]);
-  }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) sm_o[wave][lane + 64 * k] = o[k];
-  if (lane == 0) sm_l[wave] = wsum;
-  __syncthreads();
-  const float L = sm_l[0] + sm_l[1] + sm_l[2] + sm_l[3];
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    float v = sm_o[0][d] + sm_o[1][d] + sm_o[2][d] + sm_o[3][d];
-    out[(size_t)bh * D + d] = v / L;
-  }
-  if (lse && threadIdx.x == 0) lse[bh] = M + logf(L);
+  merge_splits<D, G, kWaves, false>(part_o, part_lse, S, blockIdx.x * G, out, lse);
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, int NW, bool PF>
 hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.num_splits, p.Hkv, p.B);
   switch (p.Hq / p.Hkv) {
-    case 1: decode_split_kernel<BF16, D, 1><<<grid, kThreads, 0, s>>>(p); break;
-    case 2: decode_split_kernel<BF16, D, 2><<<grid, kThreads, 0, s>>>(p); break;
-    case 4: decode_split_kernel<BF16, D, 4><<<grid, kThreads, 0, s>>>(p); break;
-    case 8: decode_split_kernel<BF16, D, 8><<<grid, kThreads, 0, s>>>(p); break;
-    case 16: decode_split_kernel<BF16, D, 16><<<grid, kThreads, 0, s>>>(p); break;
+    case 1: decode_split_kernel<BF16, D, 1, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 2: decode_split_kernel<BF16, D, 2, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 4: decode_split_kernel<BF16, D, 4, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 8: decode_split_kernel<BF16, D, 8, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 16: decode_split_kernel<BF16, D, 16, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool BF16, int D>
+hipError_t launch_nw(const DecodeParams& p, hipStream_t s) {
+  if (!p.prefetch) return launch_g<BF16, D, 4, false>(p, s);
+  switch (p.waves) {
+    case 8: return launch_g<BF16, D, 8, true>(p, s);
+    case 16: return launch_g<BF16, D, 16, true>(p, s);
+    default: return launch_g<BF16, D, 4, true>(p, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream) {
-  if (bf16) return p.D == 64 ? launch_g<true, 64>(p, stream) : launch_g<true, 128>(p, stream);
-  return p.D == 64 ? launch_g<false, 64>(p, stream) : launch_g<false, 128>(p, stream);
+  if (bf16) return p.D == 64 ? launch_nw<true, 64>(p, stream) : launch_nw<true, 128>(p, stream);
+  return p.D == 64 ? launch_nw<false, 64>(p, stream) : launch_nw<false, 128>(p, stream);
 }
 
 hipError_t launch_decode_merge(const float* part_o, const float* part_lse, int B, int Hq, int D, int S, float* out,
                                float* lse, hipStream_t stream) {
-  dim3 grid(B * Hq);
-  if (D == 64)
-    decode_merge_kernel<64><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
-  else
-    decode_merge_kernel<128><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
+  // heads are merged four at a time when Hq allows it (one workgroup each)
+  const int G = (Hq % 4 == 0) ? 4 : 1;
+  dim3 grid(B * Hq / G);
+  if (D == 64) {
+    if (G == 4) decode_merge_kernel<64, 4><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
+    else decode_merge_kernel<64, 1><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
+  } else {
+    if (G == 4) decode_merge_kernel<128, 4><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
+    else decode_merge_kernel<128, 1><<<grid, kThreads, 0, stream>>>(part_o, part_lse, S, out, lse);
+  }
   return hipGetLastError();
 }
 

@@ -74,9 +74,10 @@ float fold(float lambda, float a) { return (float)((double)lambda * (double)a); 
 
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
 
-constexpr int kDecodeRowQuantum = 16;   // split lengths are multiples of this
-constexpr int kDecodeMinRows = 256;     // shortest automatic split
-constexpr int kDecodeTargetBlocks = 1024;
+constexpr int kDecodeRowQuantum = 16;    // split lengths are multiples of this
+constexpr int kDecodeTargetWaves = 2048;  // wavefronts per decode launch the heuristic aims for
+constexpr int kDecodeMinRowsPerWave = 64; // shortest automatic share of a wavefront
+constexpr int kDecodeShortSplit = 512;    // splits this short or shorter run as "short"
 
 int round_up(int64_t x, int64_t q) { return (int)(((x + q - 1) / q) * q); }
 
@@ -183,26 +184,65 @@ yoco_status yoco_compose_kv(yoco_tensor4 k1, yoco_tensor4 ki, yoco_tensor4 v1, y
   return launched(yoco::launch_compose(p, dtype == YOCO_BF16, stream), "compose");
 }
 
+// Launch shape of the split pass. Measured on MI355X (bf16, D = 128, G = 4):
+// a launch wants about kDecodeTargetWaves wavefronts; long splits run best with
+// 4 wavefronts per workgroup and one register set (4 wavefronts per SIMD
+// resident), short splits with 8 wavefronts per workgroup and double-buffered
+// row loads, which hide the load latency that few rows per wavefront expose.
+struct DecodeShape {
+  int splits, waves;
+  bool prefetch;
+};
+
+static DecodeShape decode_shape(int B, int T, int Hkv, int S_req) {
+  DecodeShape sh;
+  const int64_t pairs = (int64_t)B * Hkv;
+  int S = S_req;
+  if (S <= 0) {
+    int64_t want = (kDecodeTargetWaves / 4 + pairs - 1) / pairs;
+    int64_t most = std::max<int64_t>(1, T / (4 * kDecodeMinRowsPerWave));
+    S = (int)std::max<int64_t>(1, std::min(want, most));
+    if (decode_rows_per_split(T, S) <= kDecodeShortSplit && S >= 2) S /= 2;   // fewer, fuller splits
+  }
+  const int rps = decode_rows_per_split(T, S);
+  sh.splits = (int)((T + (int64_t)rps - 1) / rps);   // drop splits the rounding leaves empty
+  sh.prefetch = rps <= 2 * kDecodeShortSplit;
+  sh.waves = sh.prefetch && rps >= 8 * kDecodeMinRowsPerWave ? 8 : 4;
+#ifdef YOCO_FORCE_DECODE_WAVES
+  sh.waves = YOCO_FORCE_DECODE_WAVES;
+  sh.prefetch = true;
+#endif
+  return sh;
+}
+
 int yoco_decode_num_splits(int B, int T, int Hq, int Hkv, int D) {
   (void)Hq;
   (void)D;
   if (B <= 0 || T <= 0 || Hkv <= 0) return 0;
-  int64_t pairs = (int64_t)B * Hkv;
-  int64_t want = (kDecodeTargetBlocks + pairs - 1) / pairs;
-  int64_t most = std::max<int64_t>(1, T / kDecodeMinRows);
-  int S = (int)std::max<int64_t>(1, std::min(want, most));
-  // Drop splits that the rounding of the split length would leave empty.
-  int rps = decode_rows_per_split(T, S);
-  return (int)((T + (int64_t)rps - 1) / rps);
+  return decode_shape(B, T, Hkv, 0).splits;
+}
+
+// Workspace layout: tickets [B, Hkv] u32 | part_o [B, Hq, S, D] f32 | part_lse [B, Hq, S] f32,
+// each section starting on a 16-byte boundary. The counters come first so that
+// their place does not move when the split count (or T) changes between calls.
+struct WsLayout {
+  size_t o_off, lse_off, total;
+};
+
+static WsLayout ws_layout(int B, int Hq, int Hkv, int D, int S) {
+  WsLayout w;
+  size_t rows = (size_t)B * Hq * S;
+  w.o_off = (size_t)round_up((int64_t)B * Hkv * 4, 16);
+  w.lse_off = w.o_off + rows * D * sizeof(float);
+  w.total = w.lse_off + (size_t)round_up((int64_t)(rows * sizeof(float)), 16);
+  return w;
 }
 
 size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_splits) {
   if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_splits < 0) return 0;
   int S = num_splits ? num_splits : yoco_decode_num_splits(B, T, Hq, Hkv, D);
   if (S <= 1) return 0;
-  size_t rows = (size_t)B * Hq * S;
-  size_t o_bytes = rows * D * sizeof(float);
-  return o_bytes + round_up((int64_t)(rows * sizeof(float)), 16);
+  return ws_layout(B, Hq, Hkv, D, S).total;
 }
 
 static yoco_status decode_setup(const void* q, yoco_tensor4 k, yoco_tensor4 v, const int32_t* seq_lens, int B, int T,
@@ -226,19 +266,24 @@ static yoco_status decode_setup(const void* q, yoco_tensor4 k, yoco_tensor4 v, c
   p->Hkv = Hkv;
   p->D = D;
   p->scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const DecodeShape sh = decode_shape(B, T, Hkv, S);
   p->num_splits = S;
   p->rows_per_split = decode_rows_per_split(T, S);
+  p->waves = sh.waves;
+  p->prefetch = sh.prefetch;
   p->out = nullptr;
   p->lse = nullptr;
   p->part_o = nullptr;
   p->part_lse = nullptr;
+  p->tickets = nullptr;
   if (S > 1) {
-    size_t need = yoco_decode_workspace_size(B, T, Hq, Hkv, D, S);
-    if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
-    if (ws_bytes < need) return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    WsLayout w = ws_layout(B, Hq, Hkv, D, S);
+    if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
+    if (ws_bytes < w.total) return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, w.total);
     if (!aligned16(workspace)) return fail(YOCO_ERR_ALIGNMENT, "workspace not 16-byte aligned");
-    p->part_o = static_cast<float*>(workspace);
-    p->part_lse = p->part_o + (size_t)B * Hq * S * D;
+    char* base = static_cast<char*>(workspace);
+    p->part_o = reinterpret_cast<float*>(base + w.o_off);
+    p->part_lse = reinterpret_cast<float*>(base + w.lse_off);
   }
   return YOCO_OK;
 }
@@ -259,9 +304,11 @@ yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_ten
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
   p.out = out;
   p.lse = lse;
-  hipError_t e = yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream);
-  if (e != hipSuccess || S == 1) return launched(e, "decode split pass");
-  return launched(yoco::launch_decode_merge(p.part_o, p.part_lse, B, Hq, D, S, out, lse, stream), "decode merge");
+  if (S > 1) {
+    // fused merge: the tickets live after the partials
+    p.tickets = static_cast<unsigned*>(workspace);
+  }
+  return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode");
 }
 
 yoco_status yoco_cross_attn_decode_partial(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
@@ -277,21 +324,23 @@ yoco_status yoco_cross_attn_decode_partial(const void* q, yoco_tensor4 k_cache, 
   return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode split pass");
 }
 
-yoco_status yoco_decode_merge(const void* workspace, size_t workspace_bytes, int B, int Hq, int D, int num_splits,
-                              float* out, float* lse, hipStream_t stream) {
-  if (B <= 0 || Hq <= 0 || num_splits < 2)
-    return fail(YOCO_ERR_INVALID_ARG, "B, Hq must be positive and num_splits >= 2");
+yoco_status yoco_decode_merge(const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int D,
+                              int num_splits, float* out, float* lse, hipStream_t stream) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_splits < 2)
+    return fail(YOCO_ERR_INVALID_ARG, "B, Hq, Hkv must be positive and num_splits >= 2");
+  if (Hq % Hkv) return fail(YOCO_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (D != 64 && D != 128) return fail(YOCO_ERR_UNSUPPORTED, "merge supports D in {64, 128}, got %d", D);
-  size_t rows = (size_t)B * Hq * num_splits;
-  size_t need = rows * D * sizeof(float) + rows * sizeof(float);
+  WsLayout w = ws_layout(B, Hq, Hkv, D, num_splits);
   if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL");
-  if (workspace_bytes < need) return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (workspace_bytes < w.total)
+    return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
   if (!aligned16(workspace)) return fail(YOCO_ERR_ALIGNMENT, "workspace not 16-byte aligned");
   if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
   if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
-  const float* po = static_cast<const float*>(workspace);
-  const float* pl = po + rows * D;
+  const char* base = static_cast<const char*>(workspace);
+  const float* po = reinterpret_cast<const float*>(base + w.o_off);
+  const float* pl = reinterpret_cast<const float*>(base + w.lse_off);
   return launched(yoco::launch_decode_merge(po, pl, B, Hq, D, num_splits, out, lse, stream), "decode merge");
 }
 

@@ -103,9 +103,12 @@ int yoco_decode_num_splits(int B, int T, int Hq, int Hkv, int D);
 
 /*
  * yoco_decode_workspace_size - bytes of workspace the decode needs.
- * num_splits = 0 means the automatic choice. The workspace holds the per-split
- * partial outputs [B, Hq, S, D] and log-sum-exps [B, Hq, S] in fp32.
- * Host-only; returns 0 if a size is not positive.
+ * num_splits = 0 means the automatic choice. The workspace holds one 32-bit
+ * counter per (b, kv head) [B, Hkv] first, then the per-split partial outputs
+ * [B, Hq, S, D] fp32 and their log-sum-exps [B, Hq, S] fp32, each section
+ * starting on a 16-byte boundary. The counters lead so that their place
+ * depends on B * Hkv only, not on T or the split count.
+ * Host-only; returns 0 if a size is not positive or no workspace is needed.
  */
 size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_splits);
 
@@ -122,7 +125,9 @@ size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_
  *     lse = ln sum_t exp(s_t),                g = h / (Hq / Hkv).
  * The key axis is cut into S contiguous splits that run in parallel; each
  * keeps a running (max, sum, weighted value) state and the splits are merged
- * with their log-sum-exps (an exact regrouping of the same sums).
+ * with their log-sum-exps (an exact regrouping of the same sums). The merge is
+ * fused into the same launch: the last workgroup of each (b, kv head) to
+ * finish, found with an atomic counter in the workspace, merges the splits.
  *
  *   q          [B, Hq, D] contiguous, dtype kv_dtype.
  *   k_cache, v_cache  rows [0, T) are read.
@@ -132,7 +137,12 @@ size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_
  *   out        [B, Hq, D] fp32, written.   lse  [B, Hq] fp32 natural log, or NULL.
  *   workspace  device buffer of at least yoco_decode_workspace_size(...) bytes,
  *              16-byte aligned; ignored (may be NULL) when the effective split
- *              count is 1. Its contents on entry do not matter.
+ *              count is 1. Its counter section (the first 4 * B * Hkv bytes)
+ *              must be zero before the first call that uses the workspace
+ *              (zero-fill the buffer once); every completed call leaves it zero
+ *              again, whatever T and the split count are. One workspace serves one
+ *              call at a time: calls that share a workspace must be ordered
+ *              (same stream, or synchronised).
  *   num_splits 0 = automatic; otherwise the split count S >= 1.
  *   kv_dtype   YOCO_F32 or YOCO_BF16; D in {64, 128}; Hq a multiple of Hkv,
  *              Hq / Hkv in {1, 2, 4, 8, 16}.
@@ -146,8 +156,9 @@ yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_ten
 /*
  * yoco_cross_attn_decode_partial - the split pass of yoco_cross_attn_decode alone.
  * Writes, for every (b, h, split), the split's normalised output and its
- * log-sum-exp into the workspace (an empty split gets o = 0, lse = -inf).
- * Arguments as for yoco_cross_attn_decode; num_splits must be >= 1 here.
+ * log-sum-exp into the workspace (an empty split gets o = 0, lse = -inf); the
+ * counter section is neither read nor written. Arguments as for
+ * yoco_cross_attn_decode; num_splits must be >= 2 here.
  */
 yoco_status yoco_cross_attn_decode_partial(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
                                            const int32_t* seq_lens, int B, int T, int Hq, int Hkv,
@@ -159,10 +170,10 @@ yoco_status yoco_cross_attn_decode_partial(const void* q, yoco_tensor4 k_cache, 
  * For each (b, h): M = max_s lse_s, w_s = exp(lse_s - M),
  *     o = sum_s w_s o_s / sum_s w_s,  lse = M + ln sum_s w_s.
  *   workspace  the partials written by yoco_cross_attn_decode_partial with the
- *              same B, Hq, D and num_splits (layout [B,Hq,S,D] then [B,Hq,S]).
+ *              same B, Hq, Hkv, D and num_splits (the workspace layout above).
  *   out        [B, Hq, D] fp32.   lse  [B, Hq] fp32 or NULL.
  */
-yoco_status yoco_decode_merge(const void* workspace, size_t workspace_bytes, int B, int Hq, int D,
+yoco_status yoco_decode_merge(const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int D,
                               int num_splits, float* out, float* lse, hipStream_t stream);
 
 /*

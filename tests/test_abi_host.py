@@ -116,10 +116,11 @@ def test_partial_and_merge_reject(lib):
     k = t4(BASE + (1 << 28), rows=4096)
     assert lib.yoco_cross_attn_decode_partial(BASE, k, k, None, 1, 4096, 4, 1, 128, 0.0, BASE, 1 << 30, 1, BF16,
                                               None) == INVALID
-    assert lib.yoco_decode_merge(BASE, 1 << 30, 1, 4, 96, 4, BASE, None, None) == UNSUPPORTED
-    assert lib.yoco_decode_merge(BASE, 100, 1, 4, 128, 4, BASE, None, None) == WORKSPACE
-    assert lib.yoco_decode_merge(BASE, 1 << 30, 1, 4, 128, 1, BASE, None, None) == INVALID
-    assert lib.yoco_decode_merge(None, 1 << 30, 1, 4, 128, 4, BASE, None, None) == WORKSPACE
+    assert lib.yoco_decode_merge(BASE, 1 << 30, 1, 4, 1, 96, 4, BASE, None, None) == UNSUPPORTED
+    assert lib.yoco_decode_merge(BASE, 100, 1, 4, 1, 128, 4, BASE, None, None) == WORKSPACE
+    assert lib.yoco_decode_merge(BASE, 1 << 30, 1, 4, 1, 128, 1, BASE, None, None) == INVALID
+    assert lib.yoco_decode_merge(BASE, 1 << 30, 1, 4, 3, 128, 4, BASE, None, None) == INVALID
+    assert lib.yoco_decode_merge(None, 1 << 30, 1, 4, 1, 128, 4, BASE, None, None) == WORKSPACE
 
 
 def prefill(lib, **kw):
@@ -143,13 +144,15 @@ def test_prefill_rejects(lib, kw, status):
 
 
 def test_split_heuristic_and_workspace():
-    assert Y.yoco_decode_num_splits(8, 4096, 32, 8, 128) == 16
-    assert Y.yoco_decode_num_splits(4, 131072, 32, 8, 128) == 32
-    assert Y.yoco_decode_num_splits(1, 1 << 20, 16, 4, 128) == 256
+    # launch shapes measured best on MI355X for the three decode workloads
+    assert Y.yoco_decode_num_splits(8, 4096, 32, 8, 128) == 4
+    assert Y.yoco_decode_num_splits(4, 131072, 32, 8, 128) == 16
+    assert Y.yoco_decode_num_splits(1, 1 << 20, 16, 4, 128) == 128
     assert Y.yoco_decode_num_splits(1, 256, 4, 1, 64) == 1
     assert Y.yoco_decode_num_splits(0, 256, 4, 1, 64) == 0
-    # [B, Hq, S, D] + [B, Hq, S] fp32
-    assert Y.yoco_decode_workspace_size(8, 4096, 32, 8, 128, 16) == 8 * 32 * 16 * 129 * 4
+    # [B, Hkv] u32 counters + [B, Hq, S, D] f32 + [B, Hq, S] f32, sections 16-byte aligned
+    assert Y.yoco_decode_workspace_size(8, 4096, 32, 8, 128, 16) == 8 * 8 * 4 + 8 * 32 * 16 * 129 * 4
+    assert Y.yoco_decode_workspace_size(1, 100, 3, 1, 64, 3) == 16 + 3 * 3 * 64 * 4 + 48
     assert Y.yoco_decode_workspace_size(1, 256, 4, 1, 64, 1) == 0
     for B, T, Hq, Hkv in [(3, 5, 4, 1), (1, 4097, 8, 2), (2, 100000, 16, 4)]:
         s = Y.yoco_decode_num_splits(B, T, Hq, Hkv, 128)

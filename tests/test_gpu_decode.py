@@ -151,8 +151,9 @@ def test_split_pass_and_merge_entry_points():
     Y.yoco_cross_attn_decode_partial(qd, kd, vd, ws, S_)
     torch.cuda.synchronize()
     rows = B * Hq * S_
-    part_o = host(ws[: rows * D]).reshape(B, Hq, S_, D)
-    part_l = host(ws[rows * D: rows * D + rows]).reshape(B, Hq, S_)
+    o_off = (B * Hkv * 4 + 15) // 16 * 4           # counters first, in float32 units
+    part_o = host(ws[o_off: o_off + rows * D]).reshape(B, Hq, S_, D)
+    part_l = host(ws[o_off + rows * D: o_off + rows * D + rows]).reshape(B, Hq, S_)
     rps = 256                                    # ceil(1000/4) = 250 rounded up to 16
     for s in range(S_):
         t0, t1 = s * rps, min(T, (s + 1) * rps)
@@ -160,10 +161,27 @@ def test_split_pass_and_merge_entry_points():
         _compare(part_o[:, :, s].astype(np.float64), part_l[:, :, s].astype(np.float64), o_ref, l_ref, "bf16")
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    Y.yoco_decode_merge(ws, B, Hq, D, S_, out, lse)
+    Y.yoco_decode_merge(ws, B, Hq, Hkv, D, S_, out, lse)
     torch.cuda.synchronize()
     o_ref, l_ref = O.decode_attention(q, k, v)
     _compare(host(out).astype(np.float64), host(lse).astype(np.float64), o_ref, l_ref, "bf16")
+
+
+def test_fused_merge_reuses_one_workspace():
+    """One zero-filled workspace serves successive calls whose T and split count
+    change: the counters lead the workspace and every call leaves them at zero."""
+    B, Hq, Hkv, D = 3, 8, 2, 128
+    ws = Y.decode_workspace(B, 3000, Hq, Hkv, D, 32)
+    o_off = (B * Hkv * 4 + 15) // 16 * 4
+    for i, (T, S_) in enumerate([(3000, 32), (1000, 7), (3000, 0), (64, 4), (2500, 19), (2500, 19)]):
+        q, k, v = _inputs(B, T, Hq, Hkv, D, "bf16", 70 + i)
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        Y.yoco_cross_attn_decode(dev(q), dev(k), dev(v), out, lse, num_splits=S_, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.all(ws[:o_off].view(torch.int32) == 0)
+        o_ref, lse_ref = O.decode_attention(q, k, v)
+        _compare(host(out).astype(np.float64), host(lse).astype(np.float64), o_ref, lse_ref, "bf16")
 
 
 def test_identical_keys_give_mean_value():
