@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
     ap.add_argument("--decode-splits", type=int, default=0, help="split count of the headline decodes (0: automatic)")
     ap.add_argument("--long-splits", type=int, default=0, help="split count of the long-context decodes (0: automatic)")
@@ -230,6 +230,23 @@ def leg_copy(args, torch):
     return {"bytes": nbytes, "ms": ms, "gbs": nbytes / ms / 1e6, "best_gbs": nbytes / best / 1e6}
 
 
+# ----------------------------------------------------------------- counter traffic
+
+def counter_traffic():
+    """HBM-side bytes per decode launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or None if the
+    kernel source has changed since those counters were taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(rec_path):
+        return None
+    rec = json.load(open(rec_path))
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return 1024.0 * (rec["fetch_kib_per_launch"] * rec["fetch_scale"] + rec["write_kib_per_launch"] * rec["write_scale"])
+
+
 # ----------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(args, S):
@@ -244,11 +261,11 @@ def cpu_baseline(args, S):
     w = S.DECODE_MID
     k_bits, v_bits = S.cache_kv(w)
     layer_bytes = 2 * w.B * w.T * w.Hkv * w.D * 2
+    qs = [S.queries(w, layer=l, std=w.notes["q_std"]) for l in range(w.layers)]
     layers, t_total = 0, 0.0
-    while t_total < args.cpu_seconds and layers < w.layers:
-        q = S.queries(w, layer=layers, std=w.notes["q_std"])
+    while t_total < args.cpu_seconds:      # cycle through the 16 layers until the time target
         t0 = time.perf_counter()
-        O.decode_attention(q, k_bits, v_bits)
+        O.decode_attention(qs[layers % w.layers], k_bits, v_bits)
         t_total += time.perf_counter() - t0
         layers += 1
     try:
@@ -257,7 +274,8 @@ def cpu_baseline(args, S):
         cores = os.cpu_count()
     return {"value": layers * layer_bytes / t_total / 1e9, "unit": "GB/s", "cores": threads or cores,
             "host_cores_available": cores, "kind": "oracle",
-            "sample": f"{layers} of the 16 decode layers of decode_mid_context (fp64 NumPy, {t_total:.1f} s)"}
+            "sample": f"{layers} decode-layer calls of decode_mid_context, cycling through its 16 layers "
+                      f"(fp64 NumPy, {t_total:.1f} s)"}
 
 
 def main():
@@ -292,12 +310,16 @@ def main():
     torch.cuda.synchronize()
 
     w = S.DECODE_MID
+    traffic_bytes = counter_traffic()
+    traffic = None if traffic_bytes is None else traffic_bytes / (h["decode_avg_launch_ms"] * 1e-3) / 1e9
     roofline = {"kernel": "decode_split_kernel<bf16, D=128, G=4> (split pass with fused merge)", "bound": "hbm",
                 "achieved": h["decode_warm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": h["decode_warm_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                "frac": h["decode_warm_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                "traffic_bytes_per_launch": traffic_bytes,
                 "algorithmic_bytes_per_launch": h["layer_bytes"], "avg_launch_ms": h["decode_avg_launch_ms"],
                 "note": "avg over the 16 back-to-back launches of each timed step; the 16 layers re-read one "
-                        "128 MiB cache, which fits the 256 MB Infinity Cache; flushed figure: decode_cold_gbs"}
+                        "128 MiB cache, which fits the 256 MB Infinity Cache; flushed figure: decode_cold_gbs; "
+                        "traffic: rocprofv3 FETCH_SIZE + WRITE_SIZE per launch (profiles/), in the unit of achieved"}
     line = {
         "metric": METRIC, "value": h["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
