@@ -10,7 +10,9 @@
 //
 // HBM-bound (0.5 flop per byte in bf16): every thread moves 16-byte vectors,
 // K and V of the same position are handled by the same thread in one launch,
-// and each thread keeps UNROLL independent positions in flight.
+// and each thread handles one position (deeper unrolling measured slower on
+// MI355X: fewer, longer-lived waves keep less in flight); nontemporal loads
+// and stores (temporal ones measured at about half the bandwidth).
 
 #include "common.h"
 
@@ -18,7 +20,7 @@ namespace yoco {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 1;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
