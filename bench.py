@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy")
+    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
@@ -220,6 +220,45 @@ def leg_long_decode(args, torch, Y, S, w, planted=False):
             "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBS}
 
 
+def leg_compose_on_read(args, torch, Y, S):
+    """The I/O claim of caching the composed pair: decode over the composed cache
+    (one KV set per layer) vs composing layer 1 and layer L/2 on read (two sets),
+    on the mid-context decode workload, 16 layers back to back and flushed."""
+    w = S.DECODE_MID
+    B, T, Hq, Hkv, D, L = w.B, w.T, w.Hq, w.Hkv, w.D, w.layers
+    raw = {k: up(np.ascontiguousarray(v.transpose(0, 2, 1, 3)), torch)
+           for k, v in S.compose_sources(w, layer=L // 2).items()}
+    alpha = S.alphas(w.seed, L // 2)
+    kc, vc = torch.empty_like(raw["ki"]), torch.empty_like(raw["vi"])
+    Y.yoco_compose_kv(Y.head_major(raw["k1"]), Y.head_major(raw["ki"]), Y.head_major(raw["v1"]),
+                      Y.head_major(raw["vi"]), kc, vc, 0, alpha, B=B, n=T, Hkv=Hkv, D=D, dtype=1)
+    qs = [up(S.queries(w, layer=l, std=w.notes["q_std"]), torch) for l in range(L)]
+    nsplit = Y.yoco_decode_num_splits(B, T, Hq, Hkv, D)
+    ws = Y.decode_workspace(B, T, Hq, Hkv, D, nsplit)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+
+    def stored(l=0):
+        Y.yoco_cross_attn_decode(qs[l], kc, vc, out, workspace=ws, num_splits=nsplit)
+
+    def on_read(l=0):
+        Y.yoco_cross_attn_decode_compose_on_read(qs[l], raw["k1"], raw["ki"], raw["v1"], raw["vi"], alpha, out,
+                                                 workspace=ws, num_splits=nsplit)
+
+    layer_bytes = 2 * B * T * Hkv * D * 2
+    res = {}
+    for name, fn, nbytes in (("composed_cache", stored, layer_bytes), ("compose_on_read", on_read, 2 * layer_bytes)):
+        fn()
+        warm, _ = timed(torch, lambda: [fn(l) for l in range(L)], args.reps)
+        flush = Flusher(torch)
+        cold, _ = timed(torch, fn, args.reps, flush)
+        del flush
+        res[name] = {"kv_bytes_per_layer": nbytes, "warm_ms_per_layer": warm / L, "cold_ms_per_layer": cold,
+                     "warm_gbs": nbytes / (warm / L) / 1e6, "cold_gbs": nbytes / cold / 1e6}
+    res["time_ratio_warm"] = res["compose_on_read"]["warm_ms_per_layer"] / res["composed_cache"]["warm_ms_per_layer"]
+    res["time_ratio_cold"] = res["compose_on_read"]["cold_ms_per_layer"] / res["composed_cache"]["cold_ms_per_layer"]
+    return res
+
+
 def leg_copy(args, torch):
     """A plain device-to-device copy of 1 GiB: the achievable-bandwidth reference."""
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -292,7 +331,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     Y.load_library()
-    legs = {"compose", "prefill", "long", "million", "copy"} if args.legs == "all" else \
+    legs = {"compose", "prefill", "long", "million", "copy", "cor"} if args.legs == "all" else \
         set() if args.legs == "headline" else set(args.legs.split(","))
 
     h = headline(args, torch, Y, S)
@@ -303,6 +342,8 @@ def main():
         extra["compose"] = leg_compose(args, torch, Y, S)
     if "prefill" in legs:
         extra["prefill"] = leg_prefill(args, torch, Y, S)
+    if "cor" in legs:
+        extra["compose_on_read_comparator"] = leg_compose_on_read(args, torch, Y, S)
     if "long" in legs:
         extra["decode_long_context"] = leg_long_decode(args, torch, Y, S, S.DECODE_LONG)
     if "million" in legs:

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     token_major,
     yoco_compose_kv,
     yoco_cross_attn_decode,
+    yoco_cross_attn_decode_compose_on_read,
     yoco_cross_attn_decode_partial,
     yoco_cross_attn_prefill,
     yoco_decode_merge,

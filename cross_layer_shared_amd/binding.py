@@ -20,7 +20,7 @@ YOCO_OK, YOCO_ERR_INVALID_ARG, YOCO_ERR_UNSUPPORTED, YOCO_ERR_ALIGNMENT, YOCO_ER
 YOCO_F32, YOCO_BF16 = 0, 1
 
 EXPORTED = ("yoco_compose_kv", "yoco_decode_num_splits", "yoco_decode_workspace_size", "yoco_cross_attn_decode",
-            "yoco_cross_attn_decode_partial", "yoco_decode_merge", "yoco_cross_attn_prefill", "yoco_status_string",
+            "yoco_cross_attn_decode_compose_on_read", "yoco_cross_attn_decode_partial", "yoco_decode_merge", "yoco_cross_attn_prefill", "yoco_status_string",
             "yoco_last_error", "yoco_version")
 
 
@@ -55,6 +55,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_decode_workspace_size.restype = sz
     lib.yoco_cross_attn_decode.argtypes = [vp, T4, T4, vp, i, i, i, i, i, f, vp, vp, vp, sz, i, i, vp]
     lib.yoco_cross_attn_decode.restype = st
+    lib.yoco_cross_attn_decode_compose_on_read.argtypes = [vp, T4, T4, T4, T4, vp, i, i, i, i, i, f, f, f, f, f, f,
+                                                           vp, vp, vp, sz, i, i, vp]
+    lib.yoco_cross_attn_decode_compose_on_read.restype = st
     lib.yoco_cross_attn_decode_partial.argtypes = [vp, T4, T4, vp, i, i, i, i, i, f, vp, sz, i, i, vp]
     lib.yoco_cross_attn_decode_partial.restype = st
     lib.yoco_decode_merge.argtypes = [vp, sz, i, i, i, i, i, vp, vp, vp]
@@ -169,6 +172,26 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T:
                                       out.data_ptr(), _ptr(lse), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), int(num_splits),
                                       _dtype_code(q), _stream(stream)))
+
+
+def yoco_cross_attn_decode_compose_on_read(q, k1_cache, ki_cache, v1_cache, vi_cache, alpha, out, lse=None,
+                                           lam: float = 35.0, seq_lens=None, T: int | None = None,
+                                           num_splits: int = 0, workspace: torch.Tensor | None = None,
+                                           scale: float = 0.0, stream=None) -> None:
+    """Decode over raw caches of layer 1 and layer i, composing K', V' per row on read."""
+    lib = load_library()
+    _need_contiguous(q=q, out=out, lse=lse, seq_lens=seq_lens)
+    B, Hq, D = q.shape
+    k1, ki, v1, vi = (_as_t4(x) for x in (k1_cache, ki_cache, v1_cache, vi_cache))
+    Hkv = ki_cache.shape[1]
+    T = ki.rows if T is None else T
+    if workspace is None:
+        workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
+    aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
+    _check(lib.yoco_cross_attn_decode_compose_on_read(
+        q.data_ptr(), k1, ki, v1, vi, _ptr(seq_lens), B, T, Hq, Hkv, D, float(lam), aK1, aK2, aV1, aV2, float(scale),
+        out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        int(num_splits), _dtype_code(q), _stream(stream)))
 
 
 def yoco_cross_attn_decode_partial(q, k_cache, v_cache, workspace, num_splits: int, seq_lens=None,

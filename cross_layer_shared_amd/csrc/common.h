@@ -38,6 +38,12 @@ struct DecodeParams {
   float* part_o;          // [B, Hq, S, D]   (used when num_splits > 1)
   float* part_lse;        // [B, Hq, S]
   unsigned* tickets;      // [B, Hkv] zero-initialised counters, or null (no fused merge)
+  // Compose on read (the comparator that caches the raw K_i, V_i): when set, k and
+  // v are layer i's raw caches and k1, v1 layer 1's; K' and V' are formed per row.
+  bool compose_on_read;
+  View4 k1, v1;
+  float cK1, cK2, cV1, cV2;
+  int termsK, termsV;
 };
 hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode_merge(const float* part_o, const float* part_lse, int B, int Hq, int D, int S,

@@ -1,12 +1,7 @@
 // Composition of a lower-half layer's cached KVs, written straight into the
 // cache (YOCO++ technical summary, section 2, KV composition equations; key
-// technical innovation 1: the composed K', V' are what is cached).
-//
-//   X'_i = c1 * X_1 + c2 * X_i,  c1 = fl32(lambda * a1), c2 = fl32(lambda * a2)
-//
-// computed as fma(c2, X_i, c1 * X_1) in fp32 and rounded once to the cache
-// dtype. A zero weight drops its term (and its read): with the YOCO
-// initialisation (a1 = 0, a2 = 1/lambda) the result is X_i bit for bit.
+// technical innovation 1: the composed K', V' are what is cached). The element
+// arithmetic is compose_math.h's; a zero weight also drops its read.
 //
 // HBM-bound (0.5 flop per byte in bf16): every thread moves 16-byte vectors,
 // K and V of the same position are handled by the same thread in one launch,
@@ -15,6 +10,7 @@
 // and stores (temporal ones measured at about half the bandwidth).
 
 #include "common.h"
+#include "compose_math.h"
 
 namespace yoco {
 namespace {
@@ -22,56 +18,13 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 1;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  bf16x2_t v = {(__bf16)a, (__bf16)b};  // round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Which terms are present: 3 = both, 2 = only X_i, 1 = only X_1, 0 = none (zeros).
 template <bool BF16, int TERMS>
 __device__ __forceinline__ u32x4 combine(u32x4 x1, u32x4 xi, float c1, float c2) {
-  uint32_t a[4] = {x1[0], x1[1], x1[2], x1[3]};
-  uint32_t b[4] = {xi[0], xi[1], xi[2], xi[3]};
-  uint32_t r[4];
+  u32x4 out;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (BF16) {
-      float l, h;
-      if constexpr (TERMS == 3) {
-        l = __builtin_fmaf(c2, lo_bf16(b[j]), c1 * lo_bf16(a[j]));
-        h = __builtin_fmaf(c2, hi_bf16(b[j]), c1 * hi_bf16(a[j]));
-      } else if constexpr (TERMS == 2) {
-        l = c2 * lo_bf16(b[j]);
-        h = c2 * hi_bf16(b[j]);
-      } else if constexpr (TERMS == 1) {
-        l = c1 * lo_bf16(a[j]);
-        h = c1 * hi_bf16(a[j]);
-      } else {
-        l = 0.f;
-        h = 0.f;
-      }
-      r[j] = pack_bf16(l, h);
-    } else {
-      float y;
-      if constexpr (TERMS == 3) {
-        y = __builtin_fmaf(c2, __uint_as_float(b[j]), c1 * __uint_as_float(a[j]));
-      } else if constexpr (TERMS == 2) {
-        y = c2 * __uint_as_float(b[j]);
-      } else if constexpr (TERMS == 1) {
-        y = c1 * __uint_as_float(a[j]);
-      } else {
-        y = 0.f;
-      }
-      r[j] = __float_as_uint(y);
-    }
-  }
-  u32x4 out = {r[0], r[1], r[2], r[3]};
+  for (int j = 0; j < 4; ++j) out[j] = compose_dword<BF16>(x1[j], xi[j], c1, c2, TERMS);
   return out;
 }
 
@@ -148,8 +101,6 @@ hipError_t dispatch(const Args& a, int tk, int tv, dim3 grid, hipStream_t s) {
   }
 }
 
-int terms(float c1, float c2) { return (c1 != 0.f ? 1 : 0) | (c2 != 0.f ? 2 : 0); }
-
 }  // namespace
 
 hipError_t launch_compose(const ComposeParams& p, bool bf16, hipStream_t stream) {
@@ -159,7 +110,7 @@ hipError_t launch_compose(const ComposeParams& p, bool bf16, hipStream_t stream)
   a.cpr = (uint32_t)(p.D * a.esize / 16);
   a.total = (uint32_t)((uint64_t)p.B * p.n * p.Hkv * a.cpr);
   dim3 grid((a.total + kThreads * kUnroll - 1) / (kThreads * kUnroll));
-  int tk = terms(p.cK1, p.cK2), tv = terms(p.cV1, p.cV2);
+  int tk = compose_terms(p.cK1, p.cK2), tv = compose_terms(p.cV1, p.cV2);
   return bf16 ? dispatch<true>(a, tk, tv, grid, stream) : dispatch<false>(a, tk, tv, grid, stream);
 }
 

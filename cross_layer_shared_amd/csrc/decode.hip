@@ -31,6 +31,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "compose_math.h"
 
 namespace yoco {
 namespace {
@@ -196,7 +197,7 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, c
   }
 }
 
-template <bool BF16, int D, int G, int NW, bool PREFETCH>
+template <bool BF16, int D, int G, int NW, bool PREFETCH, bool COR>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   using L = Layout<BF16, D>;
   using vec = typename L::vec;
@@ -246,6 +247,30 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
                       s * EPL * L::kES;
   const int64_t kst = p.k.st * L::kES, vst = p.v.st * L::kES;
 
+  // Compose on read: layer 1's rows are read as well and K', V' are formed per
+  // row with the compose kernel's arithmetic (two KV sets read instead of one).
+  const char* k1base = nullptr;
+  const char* v1base = nullptr;
+  int64_t k1st = 0, v1st = 0;
+  if constexpr (COR) {
+    k1base = static_cast<const char*>(p.k1.ptr) + ((int64_t)b * p.k1.sb + (int64_t)g * p.k1.sh) * L::kES +
+             s * EPL * L::kES;
+    v1base = static_cast<const char*>(p.v1.ptr) + ((int64_t)b * p.v1.sb + (int64_t)g * p.v1.sh) * L::kES +
+             s * EPL * L::kES;
+    k1st = p.k1.st * L::kES;
+    v1st = p.v1.st * L::kES;
+  }
+  auto compose_vec = [&](const vec& x1, const vec& xi, float c1, float c2, int terms) {
+    vec out;
+    if constexpr (NDW == 1) {
+      out = compose_dword<BF16>(x1, xi, c1, c2, terms);
+    } else {
+#pragma unroll
+      for (int w = 0; w < NDW; ++w) out[w] = compose_dword<BF16>(x1[w], xi[w], c1, c2, terms);
+    }
+    return out;
+  };
+
   auto load = [&](int base, vec (&kr)[U], vec (&vr)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -256,6 +281,20 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
     for (int u = 0; u < U; ++u) {
       int row = min(base + 4 * u + j, te - 1);
       vr[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(vbase + row * vst));
+    }
+    if constexpr (COR) {
+      vec k1r[U], v1r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int row = min(base + 4 * u + j, te - 1);
+        k1r[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(k1base + row * k1st));
+        v1r[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(v1base + row * v1st));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = compose_vec(k1r[u], kr[u], p.cK1, p.cK2, p.termsK);
+        vr[u] = compose_vec(v1r[u], vr[u], p.cV1, p.cV2, p.termsV);
+      }
     }
   };
 
@@ -441,18 +480,23 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __r
   merge_splits<D, G, kWaves, false>(part_o, part_lse, S, blockIdx.x * G, out, lse);
 }
 
-template <bool BF16, int D, int NW, bool PF>
-hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
+template <bool BF16, int D, int NW, bool PF, bool COR>
+hipError_t launch_gc(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.num_splits, p.Hkv, p.B);
   switch (p.Hq / p.Hkv) {
-    case 1: decode_split_kernel<BF16, D, 1, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 2: decode_split_kernel<BF16, D, 2, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 4: decode_split_kernel<BF16, D, 4, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 8: decode_split_kernel<BF16, D, 8, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 16: decode_split_kernel<BF16, D, 16, NW, PF><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 1: decode_split_kernel<BF16, D, 1, NW, PF, COR><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 2: decode_split_kernel<BF16, D, 2, NW, PF, COR><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 4: decode_split_kernel<BF16, D, 4, NW, PF, COR><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 8: decode_split_kernel<BF16, D, 8, NW, PF, COR><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 16: decode_split_kernel<BF16, D, 16, NW, PF, COR><<<grid, 64 * NW, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <bool BF16, int D, int NW, bool PF>
+hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
+  return p.compose_on_read ? launch_gc<BF16, D, NW, PF, true>(p, s) : launch_gc<BF16, D, NW, PF, false>(p, s);
 }
 
 template <bool BF16, int D>

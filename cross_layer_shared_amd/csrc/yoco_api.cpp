@@ -11,6 +11,7 @@
 
 #include "../../include/yoco.h"
 #include "common.h"
+#include "compose_math.h"
 
 namespace {
 
@@ -276,6 +277,10 @@ static yoco_status decode_setup(const void* q, yoco_tensor4 k, yoco_tensor4 v, c
   p->part_o = nullptr;
   p->part_lse = nullptr;
   p->tickets = nullptr;
+  p->compose_on_read = false;
+  p->k1 = p->v1 = yoco::View4{nullptr, 0, 0, 0};
+  p->cK1 = p->cK2 = p->cV1 = p->cV2 = 0.f;
+  p->termsK = p->termsV = 0;
   if (S > 1) {
     WsLayout w = ws_layout(B, Hq, Hkv, D, S);
     if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
@@ -309,6 +314,43 @@ yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_ten
     p.tickets = static_cast<unsigned*>(workspace);
   }
   return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode");
+}
+
+yoco_status yoco_cross_attn_decode_compose_on_read(const void* q, yoco_tensor4 k1_cache, yoco_tensor4 ki_cache,
+                                                   yoco_tensor4 v1_cache, yoco_tensor4 vi_cache,
+                                                   const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D,
+                                                   float lambda, float aK1, float aK2, float aV1, float aV2,
+                                                   float scale, float* out, float* lse, void* workspace,
+                                                   size_t workspace_bytes, int num_splits, yoco_dtype kv_dtype,
+                                                   hipStream_t stream) {
+  if (num_splits < 0) return fail(YOCO_ERR_INVALID_ARG, "num_splits must be >= 0");
+  int S = num_splits ? num_splits : yoco_decode_num_splits(B, T, Hq, Hkv, D);
+  if (S == 0) return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive");
+  yoco::DecodeParams p;
+  yoco_status st = decode_setup(q, ki_cache, vi_cache, seq_lens, B, T, Hq, Hkv, D, scale, workspace,
+                                workspace_bytes, S, kv_dtype, &p);
+  if (st != YOCO_OK) return st;
+  const size_t es = esize(kv_dtype);
+  if ((st = check_tensor("k1_cache", k1_cache, T, es)) != YOCO_OK) return st;
+  if ((st = check_tensor("v1_cache", v1_cache, T, es)) != YOCO_OK) return st;
+  if (!isfinite(lambda) || !isfinite(aK1) || !isfinite(aK2) || !isfinite(aV1) || !isfinite(aV2))
+    return fail(YOCO_ERR_INVALID_ARG, "lambda and the weights must be finite");
+  if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
+  if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
+  p.out = out;
+  p.lse = lse;
+  if (S > 1) p.tickets = static_cast<unsigned*>(workspace);
+  p.compose_on_read = true;
+  p.k1 = view(k1_cache);
+  p.v1 = view(v1_cache);
+  p.cK1 = fold(lambda, aK1);
+  p.cK2 = fold(lambda, aK2);
+  p.cV1 = fold(lambda, aV1);
+  p.cV2 = fold(lambda, aV2);
+  p.termsK = yoco::compose_terms(p.cK1, p.cK2);
+  p.termsV = yoco::compose_terms(p.cV1, p.cV2);
+  return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode (compose on read)");
 }
 
 yoco_status yoco_cross_attn_decode_partial(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,

@@ -154,6 +154,32 @@ yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_ten
                                    hipStream_t stream);
 
 /*
+ * yoco_cross_attn_decode_compose_on_read - the same decode when the cache holds
+ * the raw K_i, V_i and K_1, V_1 instead of the composed pair.
+ *
+ * The comparator for [YOCO++] key technical innovation 1 and section 3: a
+ * design that combines layers at read time (as FusedKV does, [YOCO++] section
+ * 1) must fetch two KV sets per decode step, while YOCO++ caches the composed
+ * pair and fetches one. Each row is composed on read with exactly the
+ * arithmetic of yoco_compose_kv (fl32-folded weights, one fma, one rounding),
+ * so the result equals yoco_compose_kv followed by yoco_cross_attn_decode bit
+ * for bit, at twice the cache traffic.
+ *
+ *   k1_cache, v1_cache  layer 1's K_1, V_1 (rows [0, T) read).
+ *   ki_cache, vi_cache  layer i's raw K_i, V_i (rows [0, T) read).
+ *   lambda, aK1..aV2    as for yoco_compose_kv.
+ * Other arguments, the workspace rules and the errors as for
+ * yoco_cross_attn_decode.
+ */
+yoco_status yoco_cross_attn_decode_compose_on_read(const void* q, yoco_tensor4 k1_cache, yoco_tensor4 ki_cache,
+                                                   yoco_tensor4 v1_cache, yoco_tensor4 vi_cache,
+                                                   const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D,
+                                                   float lambda, float aK1, float aK2, float aV1, float aV2,
+                                                   float scale, float* out, float* lse, void* workspace,
+                                                   size_t workspace_bytes, int num_splits, yoco_dtype kv_dtype,
+                                                   hipStream_t stream);
+
+/*
  * yoco_cross_attn_decode_partial - the split pass of yoco_cross_attn_decode alone.
  * Writes, for every (b, h, split), the split's normalised output and its
  * log-sum-exp into the workspace (an empty split gets o = 0, lse = -inf); the

@@ -123,6 +123,23 @@ def test_partial_and_merge_reject(lib):
     assert lib.yoco_decode_merge(None, 1 << 30, 1, 4, 1, 128, 4, BASE, None, None) == WORKSPACE
 
 
+def test_compose_on_read_rejects(lib):
+    k = t4(BASE + (1 << 28), rows=4096, sb=8 * 4096 * 128, sh=4096 * 128)
+
+    def call(**kw):
+        a = dict(q=BASE, k1=k, ki=k, v1=k, vi=k, B=8, T=4096, lam=35.0, a=(0.0, 0.02, 0.01, 0.03), ws=BASE + (4 << 28))
+        a.update(kw)
+        return lib.yoco_cross_attn_decode_compose_on_read(a["q"], a["k1"], a["ki"], a["v1"], a["vi"], None, a["B"],
+                                                          a["T"], 32, 8, 128, a["lam"], *a["a"], 0.0,
+                                                          BASE + (3 << 28), None, a["ws"], 1 << 30, 0, BF16, None)
+    assert call(k1=t4(0, rows=4096)) == INVALID
+    assert call(v1=t4(BASE + 8, rows=4096)) == ALIGN
+    assert call(k1=t4(BASE, rows=100)) == INVALID
+    assert call(lam=float("nan")) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(T=0) == INVALID
+
+
 def prefill(lib, **kw):
     a = dict(q=BASE, k=t4(BASE + (1 << 28), rows=8192, sb=8 * 8192 * 128, sh=8192 * 128),
              v=t4(BASE + (2 << 28), rows=8192, sb=8 * 8192 * 128, sh=8192 * 128), B=1, C=4096, p0=4096, Hq=32,
