@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor")
+    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor,backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
@@ -173,6 +173,29 @@ def leg_compose(args, torch, Y, S):
             "cold_best_gbs": bytes_per_call / best / 1e6, "back_to_back_ms": warm,
             "back_to_back_gbs": bytes_per_call / warm / 1e6,
             "hbm_frac_cold": bytes_per_call / cold / 1e6 / HBM_PEAK_GBS}
+
+
+def leg_compose_backward(args, torch, Y, S):
+    """Backward of one composed layer of the 32K-token workload ([1, 32768, 8, 128] bf16):
+    reads gk, gv, K_1, K_i, V_1, V_i, accumulates the fp32 dK_1, dV_1 and writes dK_i, dV_i."""
+    w = S.PREFILL_CHUNKED
+    B, T, Hkv, D = w.B, w.T, w.Hkv, w.D
+    src = {k: up(v, torch) for k, v in S.compose_sources(w, layer=3).items()}
+    gk = up(S.layer_source(w, "k", 4), torch).transpose(1, 2).contiguous()   # any cache-shaped gradient
+    gv = up(S.layer_source(w, "v", 4), torch).transpose(1, 2).contiguous()
+    g32 = [torch.zeros((B, T, Hkv, D), dtype=torch.float32, device="cuda") for _ in range(4)]
+    dalpha = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(4, Y.yoco_compose_backward_workspace_size(B, T, Hkv, D, 1) // 4), dtype=torch.float32,
+                     device="cuda")
+    alpha = S.alphas(w.seed, 3)
+    fn = lambda: Y.yoco_compose_kv_backward(gk, gv, 0, src["k1"], src["ki"], src["v1"], src["vi"], *g32, alpha,  # noqa
+                                            dalpha, workspace=ws)
+    fn()
+    flush = Flusher(torch)
+    ms, best = timed(torch, fn, args.reps, flush)
+    nbytes = B * T * Hkv * D * (6 * 2 + 2 * 8 + 2 * 4)
+    return {"workload": "prefill_chunked, one composed layer's backward", "bytes_per_call": nbytes, "ms": ms,
+            "gbs": nbytes / ms / 1e6, "best_gbs": nbytes / best / 1e6, "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBS}
 
 
 def leg_prefill(args, torch, Y, S):
@@ -331,7 +354,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     Y.load_library()
-    legs = {"compose", "prefill", "long", "million", "copy", "cor"} if args.legs == "all" else \
+    legs = {"compose", "prefill", "long", "million", "copy", "cor", "backward"} if args.legs == "all" else \
         set() if args.legs == "headline" else set(args.legs.split(","))
 
     h = headline(args, torch, Y, S)
@@ -340,6 +363,8 @@ def main():
         extra["copy_reference"] = leg_copy(args, torch)
     if "compose" in legs:
         extra["compose"] = leg_compose(args, torch, Y, S)
+    if "backward" in legs:
+        extra["compose_backward"] = leg_compose_backward(args, torch, Y, S)
     if "prefill" in legs:
         extra["prefill"] = leg_prefill(args, torch, Y, S)
     if "cor" in legs:

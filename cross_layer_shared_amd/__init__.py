@@ -12,7 +12,9 @@ from .binding import (  # noqa: F401
     head_major,
     load_library,
     token_major,
+    yoco_compose_backward_workspace_size,
     yoco_compose_kv,
+    yoco_compose_kv_backward,
     yoco_cross_attn_decode,
     yoco_cross_attn_decode_compose_on_read,
     yoco_cross_attn_decode_partial,

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libyoco.so")
 YOCO_OK, YOCO_ERR_INVALID_ARG, YOCO_ERR_UNSUPPORTED, YOCO_ERR_ALIGNMENT, YOCO_ERR_WORKSPACE, YOCO_ERR_LAUNCH = range(6)
 YOCO_F32, YOCO_BF16 = 0, 1
 
-EXPORTED = ("yoco_compose_kv", "yoco_decode_num_splits", "yoco_decode_workspace_size", "yoco_cross_attn_decode",
+EXPORTED = ("yoco_compose_kv", "yoco_compose_backward_workspace_size", "yoco_compose_kv_backward", "yoco_decode_num_splits", "yoco_decode_workspace_size", "yoco_cross_attn_decode",
             "yoco_cross_attn_decode_compose_on_read", "yoco_cross_attn_decode_partial", "yoco_decode_merge", "yoco_cross_attn_prefill", "yoco_status_string",
             "yoco_last_error", "yoco_version")
 
@@ -49,6 +49,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     T4, i, f, vp, sz, st = Tensor4, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.yoco_compose_kv.argtypes = [T4, T4, T4, T4, T4, T4, i, i, i, i, i, f, f, f, f, f, i, vp]
     lib.yoco_compose_kv.restype = st
+    lib.yoco_compose_backward_workspace_size.argtypes = [i, i, i, i, i]
+    lib.yoco_compose_backward_workspace_size.restype = sz
+    lib.yoco_compose_kv_backward.argtypes = [T4, T4, i, T4, T4, T4, T4, T4, T4, T4, T4, i, i, i, i, f, f, f, f, f, vp,
+                                             vp, sz, i, vp]
+    lib.yoco_compose_kv_backward.restype = st
     lib.yoco_decode_num_splits.argtypes = [i, i, i, i, i]
     lib.yoco_decode_num_splits.restype = i
     lib.yoco_decode_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -140,6 +145,30 @@ def yoco_compose_kv(k1, ki, v1, vi, k_cache, v_cache, t0: int, alpha, lam: float
     aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
     _check(lib.yoco_compose_kv(*srcs, _as_t4(k_cache), _as_t4(v_cache), int(t0), int(B), int(n), int(Hkv), int(D),
                                float(lam), aK1, aK2, aV1, aV2, int(dtype), _stream(stream)))
+
+
+def yoco_compose_backward_workspace_size(B: int, n: int, Hkv: int, D: int, dtype: int) -> int:
+    return load_library().yoco_compose_backward_workspace_size(B, n, Hkv, D, dtype)
+
+
+def yoco_compose_kv_backward(gk, gv, t0: int, k1, ki, v1, vi, dk1, dki, dv1, dvi, alpha, dalpha, lam: float = 35.0,
+                             workspace=None, stream=None) -> None:
+    """Gradients of one layer's composition. gk, gv: cache-shaped [B, Hkv, T, D] upstream
+    gradients (rows [t0, t0+n)); sources and the fp32 gradients [B, n, Hkv, D] token-major
+    (or Tensor4); dk1, dv1 accumulate, dki, dvi are written; dalpha: fp32 [4] on the device."""
+    lib = load_library()
+    B, n, Hkv, D = k1.shape
+    dtype = _dtype_code(k1)
+    if workspace is None:
+        nbytes = max(16, yoco_compose_backward_workspace_size(B, n, Hkv, D, dtype))
+        workspace = torch.empty(math.ceil(nbytes / 16) * 4, dtype=torch.float32, device=k1.device)
+    srcs = [token_major(x) for x in (k1, ki, v1, vi)]
+    grads = [token_major(x) for x in (dk1, dki, dv1, dvi)]
+    aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
+    _need_contiguous(dalpha=dalpha)
+    _check(lib.yoco_compose_kv_backward(_as_t4(gk), _as_t4(gv), int(t0), *srcs, *grads, B, n, Hkv, D, float(lam),
+                                        aK1, aK2, aV1, aV2, dalpha.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), dtype, _stream(stream)))
 
 
 def yoco_decode_num_splits(B: int, T: int, Hq: int, Hkv: int, D: int) -> int:

@@ -23,6 +23,18 @@ struct ComposeParams {
 };
 hipError_t launch_compose(const ComposeParams& p, bool bf16, hipStream_t stream);
 
+struct ComposeBackwardParams {
+  View4 gk, gv;              // upstream gradients of K', V' (rows [t0, t0 + n)), cache dtype
+  View4 k1, ki, v1, vi;      // forward sources (rows [0, n)), cache dtype
+  View4 dk1, dki, dv1, dvi;  // fp32 gradients (rows [0, n)): dk1, dv1 accumulated, dki, dvi written
+  int t0, B, n, Hkv, D;
+  float cK1, cK2, cV1, cV2;  // lambda folded into the weights (fp32)
+  float lambda;
+  float* dalpha;             // [4] fp32: daK1, daK2, daV1, daV2
+};
+int compose_backward_blocks(const ComposeBackwardParams& p, bool bf16);
+hipError_t launch_compose_backward(const ComposeBackwardParams& p, bool bf16, float* partial, hipStream_t stream);
+
 struct DecodeParams {
   const void* q;          // [B, Hq, D]
   View4 k, v;             // caches

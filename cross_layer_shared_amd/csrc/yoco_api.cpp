@@ -216,6 +216,87 @@ static DecodeShape decode_shape(int B, int T, int Hkv, int S_req) {
   return sh;
 }
 
+size_t yoco_compose_backward_workspace_size(int B, int n, int Hkv, int D, yoco_dtype dtype) {
+  if (B <= 0 || n <= 0 || Hkv <= 0 || D <= 0 || !valid_dtype(dtype)) return 0;
+  yoco::ComposeBackwardParams p{};
+  p.B = B;
+  p.n = n;
+  p.Hkv = Hkv;
+  p.D = D;
+  return (size_t)yoco::compose_backward_blocks(p, dtype == YOCO_BF16) * 4 * sizeof(float);
+}
+
+yoco_status yoco_compose_kv_backward(yoco_tensor4 gk, yoco_tensor4 gv, int t0, yoco_tensor4 k1, yoco_tensor4 ki,
+                                     yoco_tensor4 v1, yoco_tensor4 vi, yoco_tensor4 dk1, yoco_tensor4 dki,
+                                     yoco_tensor4 dv1, yoco_tensor4 dvi, int B, int n, int Hkv, int D, float lambda,
+                                     float aK1, float aK2, float aV1, float aV2, float* dalpha, void* workspace,
+                                     size_t workspace_bytes, yoco_dtype dtype, hipStream_t stream) {
+  if (B <= 0 || n <= 0 || Hkv <= 0 || D <= 0 || t0 < 0)
+    return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive and t0 >= 0 (B=%d n=%d Hkv=%d D=%d t0=%d)", B, n, Hkv,
+                D, t0);
+  if (!valid_dtype(dtype)) return fail(YOCO_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  const size_t es = esize(dtype);
+  if ((D * es) % 16 || D > 1024)
+    return fail(YOCO_ERR_UNSUPPORTED, "compose backward needs D*elemsize a multiple of 16 bytes and D <= 1024");
+  if (!isfinite(lambda) || !isfinite(aK1) || !isfinite(aK2) || !isfinite(aV1) || !isfinite(aV2))
+    return fail(YOCO_ERR_INVALID_ARG, "lambda and the weights must be finite");
+  if ((uint64_t)B * n * Hkv * (D * es / 16) >= (1ull << 31))
+    return fail(YOCO_ERR_UNSUPPORTED, "compose backward call too large (more than 2^31 16-byte vectors)");
+  yoco_status st;
+  const char* in_names[6] = {"gk", "gv", "k1", "ki", "v1", "vi"};
+  const yoco_tensor4* ins[6] = {&gk, &gv, &k1, &ki, &v1, &vi};
+  for (int i = 0; i < 6; ++i) {
+    int64_t need = i < 2 ? (int64_t)t0 + n : (int64_t)n;
+    if ((st = check_tensor(in_names[i], *ins[i], need, es)) != YOCO_OK) return st;
+  }
+  const char* out_names[4] = {"dk1", "dki", "dv1", "dvi"};
+  const yoco_tensor4* outs[4] = {&dk1, &dki, &dv1, &dvi};
+  for (int i = 0; i < 4; ++i)
+    if ((st = check_tensor(out_names[i], *outs[i], n, 4)) != YOCO_OK) return st;
+  // the four gradient outputs must not overlap one another or any input
+  for (int i = 0; i < 4; ++i) {
+    Span so = span_of(*outs[i], B, Hkv, 0, n, D, 4);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(so, span_of(*outs[j], B, Hkv, 0, n, D, 4)))
+        return fail(YOCO_ERR_INVALID_ARG, "%s overlaps %s", out_names[i], out_names[j]);
+    for (int j = 0; j < 6; ++j) {
+      int64_t r0 = j < 2 ? t0 : 0;
+      if (overlap(so, span_of(*ins[j], B, Hkv, r0, r0 + n, D, es)))
+        return fail(YOCO_ERR_INVALID_ARG, "%s overlaps %s", out_names[i], in_names[j]);
+    }
+  }
+  if (!dalpha) return fail(YOCO_ERR_INVALID_ARG, "dalpha: null pointer");
+  if (reinterpret_cast<uintptr_t>(dalpha) & 3u) return fail(YOCO_ERR_ALIGNMENT, "dalpha: not 4-byte aligned");
+  const size_t need = yoco_compose_backward_workspace_size(B, n, Hkv, D, dtype);
+  if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  if (workspace_bytes < need) return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(YOCO_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  yoco::ComposeBackwardParams p;
+  p.gk = view(gk);
+  p.gv = view(gv);
+  p.k1 = view(k1);
+  p.ki = view(ki);
+  p.v1 = view(v1);
+  p.vi = view(vi);
+  p.dk1 = view(dk1);
+  p.dki = view(dki);
+  p.dv1 = view(dv1);
+  p.dvi = view(dvi);
+  p.t0 = t0;
+  p.B = B;
+  p.n = n;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.cK1 = fold(lambda, aK1);
+  p.cK2 = fold(lambda, aK2);
+  p.cV1 = fold(lambda, aV1);
+  p.cV2 = fold(lambda, aV2);
+  p.lambda = lambda;
+  p.dalpha = dalpha;
+  return launched(yoco::launch_compose_backward(p, dtype == YOCO_BF16, static_cast<float*>(workspace), stream),
+                  "compose backward");
+}
+
 int yoco_decode_num_splits(int B, int T, int Hq, int Hkv, int D) {
   (void)Hq;
   (void)D;

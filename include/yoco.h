@@ -96,6 +96,40 @@ yoco_status yoco_compose_kv(yoco_tensor4 k1, yoco_tensor4 ki, yoco_tensor4 v1, y
                             yoco_dtype dtype, hipStream_t stream);
 
 /*
+ * yoco_compose_backward_workspace_size - bytes of workspace yoco_compose_kv_backward
+ * needs (fp32 partial sums, four per workgroup). Host-only; 0 on bad sizes.
+ */
+size_t yoco_compose_backward_workspace_size(int B, int n, int Hkv, int D, yoco_dtype dtype);
+
+/*
+ * yoco_compose_kv_backward - gradients of one layer's composition.
+ *
+ * [YOCO++] section 2: the four residual weights are learnable; innovation 2:
+ * lambda scales them. With K'_i = lambda (aK1 K_1 + aK2 K_i) and the upstream
+ * gradient gk = dL/dK'_i (likewise V):
+ *     dK_1 += c1 * gk,   dK_i = c2 * gk       (c = fl32(lambda * a), fp32),
+ *     daK1 = lambda * <gk, K_1>,   daK2 = lambda * <gk, K_i>   (and aV1, aV2).
+ *   gk, gv          upstream gradients, cache layout and dtype; rows [t0, t0+n) read.
+ *   k1, ki, v1, vi  the forward sources; rows [0, n) read.
+ *   dk1, dv1        fp32 gradients of layer 1's K, V, rows [0, n): ACCUMULATED (+=),
+ *                   so one buffer collects the contributions of every layer i.
+ *   dki, dvi        fp32 gradients of layer i's K, V, rows [0, n): written.
+ *   dalpha          device fp32 [4]: (daK1, daK2, daV1, daV2), written. The dot
+ *                   products are summed per workgroup in fp32 and across
+ *                   workgroups in fp64 in a fixed order (deterministic).
+ *   workspace       >= yoco_compose_backward_workspace_size(B, n, Hkv, D, dtype)
+ *                   bytes, 16-byte aligned; contents on entry do not matter.
+ *   dtype           YOCO_F32 or YOCO_BF16 (inputs); D * elemsize a multiple of 16.
+ * The four gradient outputs must not overlap each other or any input
+ * (YOCO_ERR_INVALID_ARG). Two kernels are enqueued on `stream`.
+ */
+yoco_status yoco_compose_kv_backward(yoco_tensor4 gk, yoco_tensor4 gv, int t0, yoco_tensor4 k1, yoco_tensor4 ki,
+                                     yoco_tensor4 v1, yoco_tensor4 vi, yoco_tensor4 dk1, yoco_tensor4 dki,
+                                     yoco_tensor4 dv1, yoco_tensor4 dvi, int B, int n, int Hkv, int D, float lambda,
+                                     float aK1, float aK2, float aV1, float aV2, float* dalpha, void* workspace,
+                                     size_t workspace_bytes, yoco_dtype dtype, hipStream_t stream);
+
+/*
  * yoco_decode_num_splits - the split count the decode picks when given 0.
  * Host-only; returns >= 1, or 0 if a size is not positive.
  */

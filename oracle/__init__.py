@@ -11,6 +11,7 @@ from .yoco_oracle import (  # noqa: F401
     bf16_nearest,
     causal_prefill,
     compose,
+    compose_backward,
     compose_kv,
     compose_magnitude,
     decode_attention,

@@ -94,6 +94,27 @@ def compose_magnitude(x1, xi, a1: float, a2: float, lam: float = LAMBDA) -> np.n
     return float(lam) * (np.abs(float(a1) * to_f64(x1)) + np.abs(float(a2) * to_f64(xi)))
 
 
+def compose_backward(gk, gv, k1, ki, v1, vi, alpha, lam: float = LAMBDA) -> dict:
+    """Gradients of one layer's composition, given the upstream gradients
+    gk = dL/dK'_i and gv = dL/dV'_i (same layout as the sources).
+
+    [YOCO++] section 2: the four residual weights are learnable and lambda is a
+    fixed scale. K'_i = lam (aK1 K_1 + aK2 K_i) is linear in every input, so
+      dL/dK_1 = lam aK1 gk,   dL/dK_i = lam aK2 gk,
+      dL/daK1 = lam <gk, K_1>,  dL/daK2 = lam <gk, K_i>,
+    and likewise for V. Returns fp64 arrays dk1, dki, dv1, dvi and the tuple
+    dalpha = (daK1, daK2, daV1, daV2)."""
+    aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
+    lam = float(lam)
+    gk64, gv64 = to_f64(gk), to_f64(gv)
+    return {
+        "dk1": lam * aK1 * gk64, "dki": lam * aK2 * gk64,
+        "dv1": lam * aV1 * gv64, "dvi": lam * aV2 * gv64,
+        "dalpha": (lam * float(np.sum(gk64 * to_f64(k1))), lam * float(np.sum(gk64 * to_f64(ki))),
+                   lam * float(np.sum(gv64 * to_f64(v1))), lam * float(np.sum(gv64 * to_f64(vi)))),
+    }
+
+
 # ---------------------------------------------------------------------------
 # O2. Decode attention over the shared cache ([YOCO] cross-decoder;
 #     [YOCO++] section 2: every upper-half layer reads K'_{L/2}, V'_{L/2}).

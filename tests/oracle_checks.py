@@ -101,6 +101,50 @@ def check_compose_kv_weights(compose_kv_fn, dtype="f32"):
                 assert np.array_equal(S.f32_to_bf16_bits(np.asarray(vp).astype(np.float32)), vw)
 
 
+# ----------------------------------------------------------------- compose backward
+
+def _loss(compose_kv_fn, gk, gv, k1, ki, v1, vi, alpha, lam=35.0):
+    kp, vp = compose_kv_fn(k1, ki, v1, vi, alpha, lam)
+    return float(np.sum(gk * kp) + np.sum(gv * vp))
+
+
+def check_compose_backward_finite_differences(backward_fn, compose_kv_fn):
+    """The composition is linear in the weights and in the sources, so central
+    differences of L = <gk, K'> + <gv, V'> give the exact gradient up to rounding."""
+    r = _rng(16)
+    shp = (2, 5, 3, 8)
+    gk, gv, k1, ki, v1, vi = (r.standard_normal(shp) for _ in range(6))
+    alpha = (0.013, -0.021, 0.034, 0.007)
+    g = backward_fn(gk, gv, k1, ki, v1, vi, alpha)
+    h = 0.5
+    for idx in range(4):
+        ap, am = list(alpha), list(alpha)
+        ap[idx] += h
+        am[idx] -= h
+        fd = (_loss(compose_kv_fn, gk, gv, k1, ki, v1, vi, ap) - _loss(compose_kv_fn, gk, gv, k1, ki, v1, vi, am)) / (2 * h)
+        assert abs(g["dalpha"][idx] - fd) <= 1e-10 * max(1.0, abs(fd))
+    for name, arr in (("dk1", k1), ("dki", ki), ("dv1", v1), ("dvi", vi)):
+        for flat in (0, 37, arr.size - 1):
+            pert = np.zeros(arr.size)
+            pert[flat] = h
+            pert = pert.reshape(arr.shape)
+            args = dict(k1=k1, ki=ki, v1=v1, vi=vi)
+            key = {"dk1": "k1", "dki": "ki", "dv1": "v1", "dvi": "vi"}[name]
+            lp = _loss(compose_kv_fn, gk, gv, **{**args, key: arr + pert}, alpha=alpha)
+            lm = _loss(compose_kv_fn, gk, gv, **{**args, key: arr - pert}, alpha=alpha)
+            fd = (lp - lm) / (2 * h)
+            assert abs(g[name].reshape(-1)[flat] - fd) <= 1e-10 * max(1.0, abs(fd))
+
+
+def check_compose_backward_identity_init(backward_fn):
+    """At a1 = 0 the layer-1 tensors get no gradient; a2 = fl32(1/35) passes gk through."""
+    r = _rng(17)
+    gk, gv, k1, ki, v1, vi = (r.standard_normal((1, 4, 2, 8)) for _ in range(6))
+    g = backward_fn(gk, gv, k1, ki, v1, vi, S.IDENTITY_ALPHA)
+    assert np.array_equal(g["dk1"], np.zeros_like(gk)) and np.array_equal(g["dv1"], np.zeros_like(gv))
+    assert np.allclose(g["dki"], gk, rtol=1e-8, atol=0) and np.allclose(g["dvi"], gv, rtol=1e-8, atol=0)
+
+
 # ----------------------------------------------------------------- decode
 
 def _qkv(B, Hq, Hkv, T, D, seed):

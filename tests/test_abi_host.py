@@ -140,6 +140,30 @@ def test_compose_on_read_rejects(lib):
     assert call(T=0) == INVALID
 
 
+def test_compose_backward_rejects(lib):
+    src = [src4(BASE + (i << 24)) for i in range(4)]
+    gk, gv = t4(BASE + (4 << 24)), t4(BASE + (5 << 24))
+    g32 = [Tensor4(BASE + ((6 + i) << 24), 256 * 8 * 128, 128, 8 * 128, 256) for i in range(4)]
+
+    def call(**kw):
+        a = dict(gk=gk, gv=gv, t0=0, src=src, g=g32, B=1, n=256, D=128, lam=35.0, dalpha=BASE + (12 << 24),
+                 ws=BASE + (13 << 24), wsb=1 << 20, dt=BF16)
+        a.update(kw)
+        return lib.yoco_compose_kv_backward(a["gk"], a["gv"], a["t0"], *a["src"], *a["g"], a["B"], a["n"], 8,
+                                            a["D"], a["lam"], 0.01, 0.02, 0.03, 0.04, a["dalpha"], a["ws"],
+                                            a["wsb"], a["dt"], None)
+    assert call(n=0) == INVALID
+    assert call(D=60) == UNSUPPORTED
+    assert call(dalpha=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    assert call(g=[g32[0], g32[0], g32[2], g32[3]]) == INVALID          # two outputs overlap
+    assert call(g=[Tensor4(src[0].ptr, 256 * 8 * 128, 128, 8 * 128, 256)] + g32[1:]) == INVALID   # output over input
+    assert call(gk=t4(BASE + (4 << 24), rows=100)) == INVALID
+    assert call(lam=float("inf")) == INVALID
+    assert Y.yoco_compose_backward_workspace_size(1, 256, 8, 128, BF16) == ((256 * 8 * 16 + 255) // 256) * 16
+
+
 def prefill(lib, **kw):
     a = dict(q=BASE, k=t4(BASE + (1 << 28), rows=8192, sb=8 * 8192 * 128, sh=8192 * 128),
              v=t4(BASE + (2 << 28), rows=8192, sb=8 * 8192 * 128, sh=8192 * 128), B=1, C=4096, p0=4096, Hq=32,

@@ -58,6 +58,32 @@ def test_compose_kv_weights(dtype):
     C.check_compose_kv_weights(O.compose_kv, dtype)
 
 
+def test_compose_backward_finite_differences():
+    C.check_compose_backward_finite_differences(O.compose_backward, O.compose_kv)
+
+
+def test_compose_backward_identity_init():
+    C.check_compose_backward_identity_init(O.compose_backward)
+
+
+@pytest.mark.parametrize("kind", ["no_lambda", "swapped_grad", "v_uses_k_weights", "sign"])
+def test_compose_backward_mutants_fail_a_pin(kind):
+    def f(gk, gv, k1, ki, v1, vi, alpha, lam=35.0):
+        g = O.compose_backward(gk, gv, k1, ki, v1, vi, alpha, lam)
+        aK1, aK2, aV1, aV2 = alpha
+        if kind == "no_lambda":
+            g["dalpha"] = tuple(x / lam for x in g["dalpha"])
+        elif kind == "swapped_grad":
+            g["dk1"], g["dki"] = g["dki"], g["dk1"]
+        elif kind == "v_uses_k_weights":
+            g["dv1"] = lam * aK1 * O.to_f64(gv)
+        elif kind == "sign":
+            g["dalpha"] = (-g["dalpha"][0],) + tuple(g["dalpha"][1:])
+        return g
+    with pytest.raises(AssertionError):
+        C.check_compose_backward_finite_differences(f, O.compose_kv)
+
+
 def test_compose_magnitude_bounds():
     k1, ki = C._pair("f32", seed=5)
     a1, a2 = 0.031, -0.047
