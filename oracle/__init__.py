@@ -15,6 +15,7 @@ from .yoco_oracle import (  # noqa: F401
     compose_kv,
     compose_magnitude,
     decode_attention,
+    self_attn_decode,
     softmax_attend,
     to_f64,
 )

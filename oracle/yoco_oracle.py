@@ -37,6 +37,9 @@ design notes of the repository):
   * Causal prefill: the query at absolute position p attends to rows [0, p]
     inclusive; the chunk only partitions query rows.
   * lse is the natural-log log-sum-exp of the scaled scores.
+  * A self-decoder decode step (the lower half keeps L/2 caches, [YOCO++]
+    section 3) composes the new token's K'_i, V'_i, which become the last
+    row n - 1 of that layer's sequence, and attends over all n rows.
 """
 from __future__ import annotations
 
@@ -181,6 +184,41 @@ def decode_attention(q, k, v, seq_lens=None, scale: float | None = None, heads=N
             ob, lb = softmax_attend(q64[b, hs], k[b, g], v[b, g], n, scale)
             o[b, hs], lse[b, hs] = ob, lb
     return o, lse
+
+
+def self_attn_decode(q, k_cache, v_cache, new_rows: dict, alpha, seq_lens=None, scale: float | None = None,
+                     lam: float = LAMBDA):
+    """One decode step of a lower-half (self-decoder) layer i.
+
+    [YOCO++] section 2: layer i caches its composed K'_i, V'_i; section 3: the
+    lower half keeps L/2 such caches, so each self-decoder layer attends over
+    its own. The new token's K'_i, V'_i are composed from its K_1, K_i, V_1,
+    V_i (``new_rows`` = {"k1", "ki", "v1", "vi"}, each [B, Hkv, D]) and become
+    row n - 1 of the sequence; the query attends over cache rows [0, n - 1)
+    followed by that row, n = seq_lens[b] (all T when None). Whatever the
+    cache holds at rows >= n - 1 is never read. Returns o [B, Hq, D],
+    lse [B, Hq] and the exact composed rows k_new, v_new [B, Hkv, D] (fp64)."""
+    q = np.asarray(q)
+    B, Hq, D = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    k_new, v_new = compose_kv(new_rows["k1"], new_rows["ki"], new_rows["v1"], new_rows["vi"], alpha, lam)
+    q64 = to_f64(q)
+    o = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        n = T if seq_lens is None else int(seq_lens[b])
+        if not 1 <= n <= T:
+            raise ValueError("seq_lens must lie in [1, T]")
+        for g in range(Hkv):
+            keys = np.concatenate([to_f64(k_cache[b, g, :n - 1]), k_new[b, g][None]])
+            vals = np.concatenate([to_f64(v_cache[b, g, :n - 1]), v_new[b, g][None]])
+            hs = slice(g * G, (g + 1) * G)
+            o[b, hs], lse[b, hs] = softmax_attend(q64[b, hs], keys, vals, n, scale)
+    return o, lse, k_new, v_new
 
 
 # ---------------------------------------------------------------------------

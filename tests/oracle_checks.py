@@ -269,6 +269,71 @@ DECODE_CHECKS = [check_decode_identical_keys, check_decode_single_token, check_d
                  check_decode_vs_sdpa, check_decode_seq_lens, check_decode_decimal, check_decode_planted_row]
 
 
+# ----------------------------------------------------------------- self-decoder decode step
+
+def _self_inputs(B, Hq, Hkv, T, D, seed):
+    """Random cache and query; the new token's four source rows are small integers."""
+    r = _rng(seed)
+    q = r.standard_normal((B, Hq, D))
+    k = r.standard_normal((B, Hkv, T, D))
+    v = r.standard_normal((B, Hkv, T, D))
+    new = {name: r.integers(-8, 9, (B, Hkv, D)).astype(np.float64) for name in ("k1", "ki", "v1", "vi")}
+    return q, k, v, new
+
+
+def check_self_decode_single_row(fn):
+    """n = 1: only the new row is attended. With lambda = 4 and weights
+    (1/4, 0) for K, (0, 1/4) for V: K' = K_1 and V' = V_i exactly, so o is V_i's
+    new row and lse = <q, K_1's new row> / sqrt(D)."""
+    q, k, v, new = _self_inputs(2, 4, 2, 5, 16, 41)
+    k[:] = 1e3
+    v[:] = -1e3
+    o, lse, kn, vn = fn(q, k, v, new, (0.25, 0.0, 0.0, 0.25), seq_lens=np.array([1, 1]), lam=4.0)
+    assert np.array_equal(kn, new["k1"]) and np.array_equal(vn, new["vi"])
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(o[b, h], new["vi"][b, h // 2])
+            assert abs(lse[b, h] - q[b, h] @ new["k1"][b, h // 2] / 4.0) < 1e-12
+
+
+def check_self_decode_reduces_to_decode(fn):
+    """With K' = K_i and V' = V_i (lambda = 4, weights (0, 1/4)) the step is
+    torch's fp64 SDPA over a cache whose row n - 1 holds the new K_i, V_i; what
+    the cache itself holds at rows >= n - 1 is never read."""
+    q, k, v, new = _self_inputs(3, 8, 2, 30, 8, 42)
+    lens = np.array([30, 7, 12])
+    k_ref, v_ref = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        k_ref[b, :, n - 1] = new["ki"][b]
+        v_ref[b, :, n - 1] = new["vi"][b]
+        k[b, :, n - 1:] = 5e2
+        v[b, :, n - 1:] = -3e2
+    o, lse, _, _ = fn(q, k, v, new, (0.0, 0.25, 0.0, 0.25), seq_lens=lens, lam=4.0)
+    o_ref, lse_ref = sdpa_reference(q, k_ref, v_ref, seq_lens=lens)
+    assert np.allclose(o, o_ref, rtol=0, atol=1e-12)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def check_self_decode_vs_sdpa(fn):
+    """lambda = 4 and weights (1/2, 1/4, -1/4, 3/4) on integer source rows, so
+    that K' = 2 K_1 + K_i and V' = -V_1 + 3 V_i exactly: torch's fp64 SDPA over
+    the cache rows followed by that row."""
+    q, k, v, new = _self_inputs(2, 4, 1, 9, 8, 43)
+    lens = np.array([9, 4])
+    k_ref, v_ref = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        k_ref[b, :, n - 1] = 2 * new["k1"][b] + new["ki"][b]
+        v_ref[b, :, n - 1] = -new["v1"][b] + 3 * new["vi"][b]
+    o, lse, kn, vn = fn(q, k, v, new, (0.5, 0.25, -0.25, 0.75), seq_lens=lens, lam=4.0)
+    assert np.array_equal(kn, 2 * new["k1"] + new["ki"]) and np.array_equal(vn, -new["v1"] + 3 * new["vi"])
+    o_ref, lse_ref = sdpa_reference(q, k_ref, v_ref, seq_lens=lens)
+    assert np.allclose(o, o_ref, rtol=0, atol=1e-12)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+SELF_DECODE_CHECKS = [check_self_decode_single_row, check_self_decode_reduces_to_decode, check_self_decode_vs_sdpa]
+
+
 # ----------------------------------------------------------------- prefill
 
 def sdpa_causal_reference(q, k, v, p0):

@@ -315,3 +315,72 @@ def test_prefill_unmutated_copy_passes():
     f = _mut_prefill("none")
     for chk in C.PREFILL_CHECKS:
         chk(f)
+
+
+def test_self_decode_pins():
+    for chk in C.SELF_DECODE_CHECKS:
+        chk(O.self_attn_decode)
+
+
+def test_self_decode_default_lambda_and_lengths():
+    """lambda defaults to 35; seq_lens None means every row; lengths outside [1, T] are rejected."""
+    q, k, v, new = C._self_inputs(1, 2, 1, 6, 8, 44)
+    inv = S.fl32(1 / 35)
+    o, _, kn, _ = O.self_attn_decode(q, k, v, new, (0.0, inv, 0.0, inv))
+    assert np.allclose(kn, new["ki"], rtol=1e-8, atol=0)
+    o2, _, _, _ = O.self_attn_decode(q, k, v, new, (0.0, inv, 0.0, inv), seq_lens=np.array([6]))
+    assert np.array_equal(o, o2)
+    with pytest.raises(ValueError):
+        O.self_attn_decode(q, k, v, new, (0.0, inv, 0.0, inv), seq_lens=np.array([7]))
+
+
+def _mut_self_decode(kind):
+    def f(q, k, v, new, alpha, seq_lens=None, scale=None, lam=35.0):
+        aK1, aK2, aV1, aV2 = alpha
+        if kind == "sources_swapped":
+            new = {"k1": new["ki"], "ki": new["k1"], "v1": new["vi"], "vi": new["v1"]}
+        if kind == "v_uses_k_weights":
+            aV1, aV2 = aK1, aK2
+        kn = lam * (aK1 * O.to_f64(new["k1"]) + aK2 * O.to_f64(new["ki"]))
+        vn = lam * (aV1 * O.to_f64(new["v1"]) + aV2 * O.to_f64(new["vi"]))
+        B, Hq, D = q.shape
+        Hkv, T = k.shape[1], k.shape[2]
+        G = Hq // Hkv
+        o, lse = np.empty((B, Hq, D)), np.empty((B, Hq))
+        for b in range(B):
+            n = T if seq_lens is None else int(seq_lens[b])
+            for h in range(Hq):
+                g = h // G
+                if kind == "new_row_from_cache":
+                    keys, vals = O.to_f64(k[b, g, :n]), O.to_f64(v[b, g, :n])
+                elif kind == "appended_after_n":
+                    keys = np.concatenate([O.to_f64(k[b, g, :n]), kn[b, g][None]])
+                    vals = np.concatenate([O.to_f64(v[b, g, :n]), vn[b, g][None]])
+                else:
+                    keys = np.concatenate([O.to_f64(k[b, g, :n - 1]), kn[b, g][None]])
+                    vals = np.concatenate([O.to_f64(v[b, g, :n - 1]), vn[b, g][None]])
+                s = keys @ O.to_f64(q[b, h]) / np.sqrt(D)
+                m = s.max()
+                p = np.exp(s - m)
+                o[b, h] = p @ vals / p.sum()
+                lse[b, h] = m + np.log(p.sum())
+        return o, lse, kn, vn
+    return f
+
+
+@pytest.mark.parametrize("kind", ["sources_swapped", "v_uses_k_weights", "new_row_from_cache", "appended_after_n"])
+def test_self_decode_mutants_fail_a_pin(kind):
+    f = _mut_self_decode(kind)
+    failed = 0
+    for chk in C.SELF_DECODE_CHECKS:
+        try:
+            chk(f)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
+
+
+def test_self_decode_unmutated_copy_passes():
+    f = _mut_self_decode("none")
+    for chk in C.SELF_DECODE_CHECKS:
+        chk(f)
