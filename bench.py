@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor,backward")
+    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor,backward,self")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
@@ -282,6 +282,53 @@ def leg_compose_on_read(args, torch, Y, S):
     return res
 
 
+def leg_self_decoder(args, torch, Y, S):
+    """One decode step of the self-decoder half on the mid-context decode workload:
+    L/2 = 16 layers, each attending over its own composed cache (16 distinct
+    128 MiB caches, so no layer finds the previous one's rows in the Infinity
+    Cache). Fused: one launch per layer composes the new token's row, appends it
+    and attends. Unfused: compose (n=1) then decode, two launches per layer."""
+    w = S.DECODE_MID
+    B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
+    half = w.layers          # the self-decoder half has as many layers as the cross-decoder half
+    k_bits, v_bits = S.cache_kv(w)
+    k0, v0 = up(k_bits, torch), up(v_bits, torch)
+    caches = [(k0.clone(), v0.clone()) for _ in range(half)]
+    del k0, v0
+    qs = [up(S.queries(w, layer=l, std=w.notes["q_std"]), torch) for l in range(half)]
+    srcs = []
+    for l in range(1, half + 1):
+        new = S.compose_sources(w, layer=l, n=1)
+        srcs.append({k: up(v, torch) for k, v in new.items()})              # [B, 1, Hkv, D]
+    alphas = [S.IDENTITY_ALPHA if l == 1 else S.alphas(w.seed, l) for l in range(1, half + 1)]
+    nsplit = Y.yoco_decode_num_splits(B, T, Hq, Hkv, D)
+    ws = Y.decode_workspace(B, T, Hq, Hkv, D, nsplit)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+
+    def fused():
+        for l in range(half):
+            s, (kc, vc) = srcs[l], caches[l]
+            Y.yoco_self_attn_decode(qs[l], s["k1"][:, 0], s["ki"][:, 0], s["v1"][:, 0], s["vi"][:, 0], kc, vc,
+                                    alphas[l], out, workspace=ws, num_splits=nsplit)
+
+    def unfused():
+        for l in range(half):
+            s, (kc, vc) = srcs[l], caches[l]
+            Y.yoco_compose_kv(s["k1"], s["ki"], s["v1"], s["vi"], kc, vc, T - 1, alphas[l])
+            Y.yoco_cross_attn_decode(qs[l], kc, vc, out, workspace=ws, num_splits=nsplit)
+
+    layer_bytes = 2 * B * T * Hkv * D * 2
+    res = {"layers": half, "kv_bytes_per_layer": layer_bytes}
+    for name, fn in (("fused", fused), ("compose_then_decode", unfused)):
+        fn()
+        ms, best = timed(torch, fn, args.reps)
+        res[name] = {"ms_per_step": ms, "gbs": half * layer_bytes / ms / 1e6,
+                     "best_gbs": half * layer_bytes / best / 1e6}
+    res["speedup_fused"] = res["compose_then_decode"]["ms_per_step"] / res["fused"]["ms_per_step"]
+    del caches
+    return res
+
+
 def leg_copy(args, torch):
     """A plain device-to-device copy of 1 GiB: the achievable-bandwidth reference."""
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -354,7 +401,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     Y.load_library()
-    legs = {"compose", "prefill", "long", "million", "copy", "cor", "backward"} if args.legs == "all" else \
+    legs = {"compose", "prefill", "long", "million", "copy", "cor", "backward", "self"} if args.legs == "all" else \
         set() if args.legs == "headline" else set(args.legs.split(","))
 
     h = headline(args, torch, Y, S)
@@ -369,6 +416,8 @@ def main():
         extra["prefill"] = leg_prefill(args, torch, Y, S)
     if "cor" in legs:
         extra["compose_on_read_comparator"] = leg_compose_on_read(args, torch, Y, S)
+    if "self" in legs:
+        extra["self_decoder_step"] = leg_self_decoder(args, torch, Y, S)
     if "long" in legs:
         extra["decode_long_context"] = leg_long_decode(args, torch, Y, S, S.DECODE_LONG)
     if "million" in legs:

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     decode_workspace,
     head_major,
     load_library,
+    one_token,
     token_major,
     yoco_compose_backward_workspace_size,
     yoco_compose_kv,
@@ -23,6 +24,7 @@ from .binding import (  # noqa: F401
     yoco_decode_num_splits,
     yoco_decode_workspace_size,
     yoco_last_error,
+    yoco_self_attn_decode,
     yoco_status_string,
     yoco_version,
 )

@@ -20,7 +20,7 @@ YOCO_OK, YOCO_ERR_INVALID_ARG, YOCO_ERR_UNSUPPORTED, YOCO_ERR_ALIGNMENT, YOCO_ER
 YOCO_F32, YOCO_BF16 = 0, 1
 
 EXPORTED = ("yoco_compose_kv", "yoco_compose_backward_workspace_size", "yoco_compose_kv_backward", "yoco_decode_num_splits", "yoco_decode_workspace_size", "yoco_cross_attn_decode",
-            "yoco_cross_attn_decode_compose_on_read", "yoco_cross_attn_decode_partial", "yoco_decode_merge", "yoco_cross_attn_prefill", "yoco_status_string",
+            "yoco_cross_attn_decode_compose_on_read", "yoco_self_attn_decode", "yoco_cross_attn_decode_partial", "yoco_decode_merge", "yoco_cross_attn_prefill", "yoco_status_string",
             "yoco_last_error", "yoco_version")
 
 
@@ -63,6 +63,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_cross_attn_decode_compose_on_read.argtypes = [vp, T4, T4, T4, T4, vp, i, i, i, i, i, f, f, f, f, f, f,
                                                            vp, vp, vp, sz, i, i, vp]
     lib.yoco_cross_attn_decode_compose_on_read.restype = st
+    lib.yoco_self_attn_decode.argtypes = [vp, T4, T4, T4, T4, T4, T4, vp, i, i, i, i, i, f, f, f, f, f, f, vp, vp,
+                                          vp, sz, i, i, vp]
+    lib.yoco_self_attn_decode.restype = st
     lib.yoco_cross_attn_decode_partial.argtypes = [vp, T4, T4, vp, i, i, i, i, i, f, vp, sz, i, i, vp]
     lib.yoco_cross_attn_decode_partial.restype = st
     lib.yoco_decode_merge.argtypes = [vp, sz, i, i, i, i, i, vp, vp, vp]
@@ -220,6 +223,41 @@ def yoco_cross_attn_decode_compose_on_read(q, k1_cache, ki_cache, v1_cache, vi_c
     _check(lib.yoco_cross_attn_decode_compose_on_read(
         q.data_ptr(), k1, ki, v1, vi, _ptr(seq_lens), B, T, Hq, Hkv, D, float(lam), aK1, aK2, aV1, aV2, float(scale),
         out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        int(num_splits), _dtype_code(q), _stream(stream)))
+
+
+def one_token(t: torch.Tensor) -> Tensor4:
+    """[B, H, D] (D contiguous), the rows of one token -> Tensor4 with stride_t = 0."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("expected a [B, H, D] tensor with a contiguous last axis")
+    return Tensor4(t.data_ptr(), t.stride(0), t.stride(1), 0, 1)
+
+
+def _source_t4(x) -> Tensor4:
+    if isinstance(x, Tensor4):
+        return x
+    return one_token(x) if x.dim() == 3 else head_major(x)
+
+
+def yoco_self_attn_decode(q, k1_new, ki_new, v1_new, vi_new, k_cache, v_cache, alpha, out, lse=None,
+                          lam: float = 35.0, seq_lens=None, T: int | None = None, num_splits: int = 0,
+                          workspace: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> None:
+    """Self-decoder decode step of layer i: compose the new token's K', V' (sources [B, Hkv, D]
+    one-token tensors, [B, Hkv, T, D] caches read at row seq_len-1, or Tensor4), write them at
+    row seq_len-1 of k_cache, v_cache [B, Hkv, T, D] and attend over rows [0, seq_len)."""
+    lib = load_library()
+    _need_contiguous(q=q, out=out, lse=lse, seq_lens=seq_lens)
+    B, Hq, D = q.shape
+    srcs = [_source_t4(x) for x in (k1_new, ki_new, v1_new, vi_new)]
+    kc, vc = _as_t4(k_cache), _as_t4(v_cache)
+    Hkv = k_cache.shape[1]
+    T = kc.rows if T is None else T
+    if workspace is None:
+        workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
+    aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
+    _check(lib.yoco_self_attn_decode(
+        q.data_ptr(), *srcs, kc, vc, _ptr(seq_lens), B, T, Hq, Hkv, D, float(lam), aK1, aK2, aV1, aV2,
+        float(scale), out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         int(num_splits), _dtype_code(q), _stream(stream)))
 
 

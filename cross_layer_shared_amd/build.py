@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libyoco.so")
-SOURCES = ["yoco_api.cpp", "compose.hip", "compose_backward.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["yoco_api.cpp", "compose.hip", "compose_backward.hip", "decode.hip", "decode_cor.hip", "decode_append.hip",
+           "prefill.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are switched off for the device code (the target

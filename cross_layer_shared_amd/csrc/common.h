@@ -54,6 +54,11 @@ struct DecodeParams {
   // v are layer i's raw caches and k1, v1 layer 1's; K' and V' are formed per row.
   bool compose_on_read;
   View4 k1, v1;
+  // Self-decoder step (append): the new token's source rows, read at row
+  // seq_len - 1 of each view (stride_t = 0 for a one-token buffer); the composed
+  // row is written into k, v at that row. Shares the folded weights below.
+  bool append;
+  View4 nk1, nki, nv1, nvi;
   float cK1, cK2, cV1, cV2;
   int termsK, termsV;
 };

@@ -360,6 +360,8 @@ static yoco_status decode_setup(const void* q, yoco_tensor4 k, yoco_tensor4 v, c
   p->tickets = nullptr;
   p->compose_on_read = false;
   p->k1 = p->v1 = yoco::View4{nullptr, 0, 0, 0};
+  p->append = false;
+  p->nk1 = p->nki = p->nv1 = p->nvi = yoco::View4{nullptr, 0, 0, 0};
   p->cK1 = p->cK2 = p->cV1 = p->cV2 = 0.f;
   p->termsK = p->termsV = 0;
   if (S > 1) {
@@ -432,6 +434,63 @@ yoco_status yoco_cross_attn_decode_compose_on_read(const void* q, yoco_tensor4 k
   p.termsK = yoco::compose_terms(p.cK1, p.cK2);
   p.termsV = yoco::compose_terms(p.cV1, p.cV2);
   return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode (compose on read)");
+}
+
+yoco_status yoco_self_attn_decode(const void* q, yoco_tensor4 k1_new, yoco_tensor4 ki_new, yoco_tensor4 v1_new,
+                                  yoco_tensor4 vi_new, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
+                                  const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D, float lambda,
+                                  float aK1, float aK2, float aV1, float aV2, float scale, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, int num_splits, yoco_dtype kv_dtype,
+                                  hipStream_t stream) {
+  if (num_splits < 0) return fail(YOCO_ERR_INVALID_ARG, "num_splits must be >= 0");
+  int S = num_splits ? num_splits : yoco_decode_num_splits(B, T, Hq, Hkv, D);
+  if (S == 0) return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive");
+  yoco::DecodeParams p;
+  yoco_status st =
+      decode_setup(q, k_cache, v_cache, seq_lens, B, T, Hq, Hkv, D, scale, workspace, workspace_bytes, S, kv_dtype, &p);
+  if (st != YOCO_OK) return st;
+  if (!isfinite(lambda) || !isfinite(aK1) || !isfinite(aK2) || !isfinite(aV1) || !isfinite(aV2))
+    return fail(YOCO_ERR_INVALID_ARG, "lambda and the weights must be finite");
+  const size_t es = esize(kv_dtype);
+  const char* names[4] = {"k1_new", "ki_new", "v1_new", "vi_new"};
+  const yoco_tensor4* src[4] = {&k1_new, &ki_new, &v1_new, &vi_new};
+  for (int i = 0; i < 4; ++i) {
+    // a source is read at row seq_len - 1 <= T - 1; a one-token buffer has stride_t = 0
+    const int64_t need = src[i]->stride_t == 0 ? 1 : T;
+    if ((st = check_tensor(names[i], *src[i], need, es)) != YOCO_OK) return st;
+    // The cache is read at rows below seq_len - 1 and written at that row, so a
+    // source may share its memory only as the very same view (in-place compose).
+    const yoco_tensor4& c = i < 2 ? k_cache : v_cache;
+    const yoco_tensor4& c_other = i < 2 ? v_cache : k_cache;
+    const bool same = src[i]->ptr == c.ptr && src[i]->stride_b == c.stride_b && src[i]->stride_h == c.stride_h &&
+                      src[i]->stride_t == c.stride_t;
+    const Span ss = span_of(*src[i], B, Hkv, 0, src[i]->stride_t == 0 ? 1 : T, D, es);
+    if (!same && overlap(ss, span_of(c, B, Hkv, 0, T, D, es)))
+      return fail(YOCO_ERR_INVALID_ARG, "%s overlaps %s without being the same view", names[i],
+                  i < 2 ? "k_cache" : "v_cache");
+    if (overlap(ss, span_of(c_other, B, Hkv, 0, T, D, es)))
+      return fail(YOCO_ERR_INVALID_ARG, "%s overlaps %s", names[i], i < 2 ? "v_cache" : "k_cache");
+  }
+  if (overlap(span_of(k_cache, B, Hkv, 0, T, D, es), span_of(v_cache, B, Hkv, 0, T, D, es)))
+    return fail(YOCO_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+  if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
+  if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
+  p.out = out;
+  p.lse = lse;
+  if (S > 1) p.tickets = static_cast<unsigned*>(workspace);
+  p.append = true;
+  p.nk1 = view(k1_new);
+  p.nki = view(ki_new);
+  p.nv1 = view(v1_new);
+  p.nvi = view(vi_new);
+  p.cK1 = fold(lambda, aK1);
+  p.cK2 = fold(lambda, aK2);
+  p.cV1 = fold(lambda, aV1);
+  p.cV2 = fold(lambda, aV2);
+  p.termsK = yoco::compose_terms(p.cK1, p.cK2);
+  p.termsV = yoco::compose_terms(p.cV1, p.cV2);
+  return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "self-decoder decode step");
 }
 
 yoco_status yoco_cross_attn_decode_partial(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,

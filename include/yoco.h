@@ -214,6 +214,43 @@ yoco_status yoco_cross_attn_decode_compose_on_read(const void* q, yoco_tensor4 k
                                                    hipStream_t stream);
 
 /*
+ * yoco_self_attn_decode - one decode step of a lower-half (self-decoder) layer i:
+ * compose the new token's K'_i, V'_i, append them to the layer's own cache and
+ * attend over the whole sequence.
+ *
+ * [YOCO++] section 2 (KV composition; the composed pair is what layer i caches)
+ * and section 3 (the lower half keeps L/2 caches, one per layer). For each
+ * sequence b with n = seq_lens[b] (T when seq_lens is NULL; clamped to [1, T]):
+ *     K'_new = fl(c_K1 K_1,new + c_K2 K_i,new),  V'_new likewise
+ * (fl32-folded weights and one rounding, bit for bit yoco_compose_kv), written
+ * into k_cache, v_cache at row n - 1; then the query attends over cache rows
+ * [0, n - 1) and the new row, as yoco_cross_attn_decode does over n rows.
+ * The cache's old contents at row n - 1 are never read.
+ *
+ *   k1_new, ki_new, v1_new, vi_new
+ *              the new token's K_1, K_i, V_1, V_i, element (b, g, :) read at
+ *              row n - 1 of each view. A buffer holding only the new token
+ *              ([B, Hkv, D] or [B, 1, Hkv, D]) is passed with stride_t = 0 and
+ *              rows >= 1; otherwise rows >= T. K_1's row is usually layer 1's
+ *              own cache, which holds K_1 unchanged. A source may be the very
+ *              same view as its destination cache (in-place compose of a row
+ *              already written there raw); any other overlap with either
+ *              cache is YOCO_ERR_INVALID_ARG.
+ *   k_cache, v_cache  layer i's composed caches: rows [0, n - 1) read, row
+ *              n - 1 written.
+ *   lambda, aK1..aV2  as for yoco_compose_kv.
+ * Other arguments, the workspace rules and the errors as for
+ * yoco_cross_attn_decode. Launches on stream; the written rows are visible to
+ * later work on that stream.
+ */
+yoco_status yoco_self_attn_decode(const void* q, yoco_tensor4 k1_new, yoco_tensor4 ki_new, yoco_tensor4 v1_new,
+                                  yoco_tensor4 vi_new, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
+                                  const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D, float lambda,
+                                  float aK1, float aK2, float aV1, float aV2, float scale, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, int num_splits, yoco_dtype kv_dtype,
+                                  hipStream_t stream);
+
+/*
  * yoco_cross_attn_decode_partial - the split pass of yoco_cross_attn_decode alone.
  * Writes, for every (b, h, split), the split's normalised output and its
  * log-sum-exp into the workspace (an empty split gets o = 0, lse = -inf); the

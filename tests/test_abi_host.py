@@ -140,6 +140,30 @@ def test_compose_on_read_rejects(lib):
     assert call(T=0) == INVALID
 
 
+def test_self_attn_decode_rejects(lib):
+    kc = t4(BASE + (1 << 28), rows=4096, sb=8 * 4096 * 128, sh=4096 * 128)
+    vc = t4(BASE + (2 << 28), rows=4096, sb=8 * 4096 * 128, sh=4096 * 128)
+    one = t4(BASE + (5 << 28), sb=8 * 128, sh=128, st=0, rows=1)      # [B, Hkv, D] one-token rows
+
+    def call(**kw):
+        a = dict(q=BASE, k1=one, ki=one, v1=one, vi=one, kc=kc, vc=vc, B=8, T=4096, lam=35.0,
+                 a=(0.0, 0.02, 0.01, 0.03), ws=BASE + (4 << 28))
+        a.update(kw)
+        return lib.yoco_self_attn_decode(a["q"], a["k1"], a["ki"], a["v1"], a["vi"], a["kc"], a["vc"], None, a["B"],
+                                         a["T"], 32, 8, 128, a["lam"], *a["a"], 0.0, BASE + (3 << 28), None, a["ws"],
+                                         1 << 30, 0, BF16, None)
+    assert call(k1=t4(0, st=0, rows=1)) == INVALID                                  # null source
+    assert call(v1=t4(BASE + (5 << 28) + 8, sb=8 * 128, sh=128, st=0, rows=1)) == ALIGN
+    assert call(ki=t4(BASE + (6 << 28), rows=100)) == INVALID                       # too few rows, stride_t != 0
+    # a source inside a cache without being the same view, or inside the other cache
+    assert call(ki=t4(BASE + (1 << 28) + 4096 * 128 * 2, rows=4096, sb=8 * 4096 * 128, sh=4096 * 128)) == INVALID
+    assert call(vi=t4(BASE + (1 << 28), sb=8 * 128, sh=128, st=0, rows=1)) == INVALID
+    assert call(vc=kc) == INVALID                                                   # caches overlap
+    assert call(lam=float("inf")) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(T=0) == INVALID
+
+
 def test_compose_backward_rejects(lib):
     src = [src4(BASE + (i << 24)) for i in range(4)]
     gk, gv = t4(BASE + (4 << 24)), t4(BASE + (5 << 24))
