@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor,backward,self")
+    ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor,backward,self,early_exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
@@ -329,6 +329,64 @@ def leg_self_decoder(args, torch, Y, S):
     return res
 
 
+def leg_early_exit(args, torch, Y, S):
+    """The prefill of the 32K-token workload (1 x 32768 tokens, 32/8 heads, D=128)
+    through the cache path, with and without YOCO's early exit. Both compose the
+    15 composed self-decoder layers (i = 2..16) for all T rows. With the early
+    exit the 16 cross-decoder layers then run only for the last token (one
+    decode call each over the shared K'_16, V'_16); without it each cross layer
+    runs the full causal chunked prefill (8 chunks of 4096). The decode of the
+    last token and the last prefill row are reported side by side (they must agree)."""
+    w = S.PREFILL_CHUNKED
+    B, T, Hq, Hkv, D, C = w.B, w.T, w.Hq, w.Hkv, w.D, w.chunk
+    cross = w.self_layers                       # as many cross-decoder layers as self-decoder layers
+    k1 = up(S.layer_source(w, "k", 1), torch)
+    v1 = up(S.layer_source(w, "v", 1), torch)
+    ki0 = up(S.layer_source(w, "k", 2), torch)
+    vi0 = up(S.layer_source(w, "v", 2), torch)
+    layers = list(range(2, w.self_layers + 1))
+    # one layer's sources drawn on the host, copied on the device for the others:
+    # distinct memory, so no compose finds its inputs in the Infinity Cache
+    srcs = [(ki0, vi0)] + [(ki0.clone(), vi0.clone()) for _ in layers[1:]]
+    caches = [(torch.empty((B, Hkv, T, D), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, Hkv, T, D), dtype=torch.bfloat16, device="cuda")) for _ in layers]
+    alphas = [S.alphas(w.seed, i) for i in layers]
+    kc, vc = caches[-1]                          # K'_{L/2}, V'_{L/2}: what every cross layer reads
+    q = up(S.queries(w, rows=T), torch)
+    q_last = q[:, T - 1].contiguous()
+    nsplit = Y.yoco_decode_num_splits(B, T, Hq, Hkv, D)
+    ws = Y.decode_workspace(B, T, Hq, Hkv, D, nsplit)
+    out_dec = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    out_pf = torch.empty((B, C, Hq, D), dtype=torch.float32, device="cuda")
+
+    def compose_all():
+        for (ki, vi), (kcl, vcl), a in zip(srcs, caches, alphas):
+            Y.yoco_compose_kv(k1, ki, v1, vi, kcl, vcl, 0, a)
+
+    def early_exit():
+        compose_all()
+        for _ in range(cross):
+            Y.yoco_cross_attn_decode(q_last, kc, vc, out_dec, workspace=ws, num_splits=nsplit)
+
+    def full():
+        compose_all()
+        for _ in range(cross):
+            for c0 in range(0, T, C):
+                Y.yoco_cross_attn_prefill(q[:, c0:c0 + C], kc, vc, c0, out_pf)
+
+    early_exit()
+    full()
+    torch.cuda.synchronize()
+    agree = float((out_pf[:, C - 1] - out_dec).abs().max())
+    ee_ms, ee_best = timed(torch, early_exit, args.reps)
+    full_ms, _ = timed(torch, full, 2)
+    compose_ms, _ = timed(torch, compose_all, args.reps)
+    return {"cross_layers": cross, "composed_layers": len(layers), "early_exit_ms": ee_ms,
+            "early_exit_best_ms": ee_best, "without_early_exit_ms": full_ms, "compose_only_ms": compose_ms,
+            "cross_part_early_exit_ms": ee_ms - compose_ms, "cross_part_full_ms": full_ms - compose_ms,
+            "speedup": full_ms / ee_ms, "max_abs_last_row_decode_vs_prefill": agree}
+
+
 def leg_copy(args, torch):
     """A plain device-to-device copy of 1 GiB: the achievable-bandwidth reference."""
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -401,7 +459,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     Y.load_library()
-    legs = {"compose", "prefill", "long", "million", "copy", "cor", "backward", "self"} if args.legs == "all" else \
+    legs = {"compose", "prefill", "long", "million", "copy", "cor", "backward", "self", "early_exit"} if args.legs == "all" else \
         set() if args.legs == "headline" else set(args.legs.split(","))
 
     h = headline(args, torch, Y, S)
@@ -418,6 +476,8 @@ def main():
         extra["compose_on_read_comparator"] = leg_compose_on_read(args, torch, Y, S)
     if "self" in legs:
         extra["self_decoder_step"] = leg_self_decoder(args, torch, Y, S)
+    if "early_exit" in legs:
+        extra["early_exit_prefill"] = leg_early_exit(args, torch, Y, S)
     if "long" in legs:
         extra["decode_long_context"] = leg_long_decode(args, torch, Y, S, S.DECODE_LONG)
     if "million" in legs:
