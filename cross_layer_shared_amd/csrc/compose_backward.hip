@@ -7,12 +7,16 @@
 //   daK1 = lambda * <gk, K_1>,  daK2 = lambda * <gk, K_i>,
 //
 // and likewise for V. HBM-bound: per element position it reads gk, gv, K_1,
-// K_i, V_1, V_i (nontemporal), reads-modifies-writes the two accumulated fp32
-// gradients (temporal: a nontemporal read-modify-write measured slower on
-// MI355X) and writes the other two (nontemporal). The weight gradients are
-// dot products over all positions: each workgroup
-// writes its four fp32 partial sums, and a second kernel adds the partials in
-// a fixed order in fp64 (deterministic).
+// K_i, V_1, V_i, reads-modifies-writes the two accumulated fp32 gradients and
+// writes the other two, all with nontemporal accesses. A thread handles four
+// consecutive elements, so that every access instruction of a wavefront
+// covers one contiguous span (a store pattern that leaves holes in each
+// 32-byte sector is written back sector by sector, doubling the write
+// traffic). The weight gradients are dot products over all positions: each
+// workgroup writes its four fp32 partial sums, and a second kernel adds the
+// partials in a fixed order in fp64 (deterministic).
+
+#include <type_traits>
 
 #include "common.h"
 #include "compose_math.h"
@@ -21,87 +25,116 @@ namespace yoco {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kVecPerThread = 4;   // four-element vectors per thread, loads issued together
+constexpr int kFinishThreads = 1024;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ const char* elem(const View4& v, int b, int h, int t, int es) {
-  return static_cast<const char*>(v.ptr) + ((int64_t)b * v.sb + (int64_t)h * v.sh + (int64_t)t * v.st) * es;
-}
-
-// Unpack one 16-byte vector of stored values into fp32.
 template <bool BF16>
-__device__ __forceinline__ void unpack(const u32x4& w, float (&x)[BF16 ? 8 : 4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
+struct Src {
+  typedef typename std::conditional<BF16, u32x2, u32x4>::type vec;   // four stored elements
+  static constexpr int kES = BF16 ? 2 : 4;
+  __device__ __forceinline__ static f32x4 unpack(const vec& w) {
+    f32x4 x;
     if constexpr (BF16) {
-      x[2 * j] = bf16_lo(w[j]);
-      x[2 * j + 1] = bf16_hi(w[j]);
+      x[0] = bf16_lo(w[0]);
+      x[1] = bf16_hi(w[0]);
+      x[2] = bf16_lo(w[1]);
+      x[3] = bf16_hi(w[1]);
     } else {
-      x[j] = __uint_as_float(w[j]);
+      x[0] = __uint_as_float(w[0]);
+      x[1] = __uint_as_float(w[1]);
+      x[2] = __uint_as_float(w[2]);
+      x[3] = __uint_as_float(w[3]);
     }
+    return x;
   }
+};
+
+__device__ __forceinline__ int64_t off(const View4& v, int b, int h, int t) {
+  return (int64_t)b * v.sb + (int64_t)h * v.sh + (int64_t)t * v.st;
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void compose_backward_kernel(ComposeBackwardParams p, uint32_t cpr,
                                                                     uint32_t total, float* __restrict__ partial) {
-  constexpr int E = BF16 ? 8 : 4;      // elements per 16-byte source vector
-  constexpr int ES = BF16 ? 2 : 4;
+  using SV = Src<BF16>;
+  using vec = typename SV::vec;
   float sk1 = 0.f, ski = 0.f, sv1 = 0.f, svi = 0.f;
-  const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
-  if (idx < total) {
-    const uint32_t c = idx % cpr;
-    uint32_t r = idx / cpr;
+  const uint32_t first = blockIdx.x * (kThreads * kVecPerThread) + threadIdx.x;
+  vec gk[kVecPerThread], gv[kVecPerThread], k1[kVecPerThread], ki[kVecPerThread], v1[kVecPerThread],
+      vi[kVecPerThread];
+  f32x4 a1[kVecPerThread], b1[kVecPerThread];
+  f32x4* dk1p[kVecPerThread];
+  f32x4* dv1p[kVecPerThread];
+  f32x4* dkip[kVecPerThread];
+  f32x4* dvip[kVecPerThread];
+  bool live[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const uint32_t idx = first + u * kThreads;
+    live[u] = idx < total;
+    const uint32_t i = live[u] ? idx : total - 1;     // clamped: loads stay in bounds, results unused
+    const uint32_t c = i % cpr;
+    uint32_t r = i / cpr;
     const int h = (int)(r % (uint32_t)p.Hkv);
     r /= (uint32_t)p.Hkv;
     const int t = (int)(r % (uint32_t)p.n);
     const int b = (int)(r / (uint32_t)p.n);
     auto ld = [&](const View4& v, int row) {
-      return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(elem(v, b, h, row, ES)) + c);
+      return __builtin_nontemporal_load(reinterpret_cast<const vec*>(static_cast<const char*>(v.ptr) +
+                                                                     off(v, b, h, row) * SV::kES) + c);
     };
-    float gk[E], gv[E], k1[E], ki[E], v1[E], vi[E];
-    unpack<BF16>(ld(p.gk, p.t0 + t), gk);
-    unpack<BF16>(ld(p.gv, p.t0 + t), gv);
-    unpack<BF16>(ld(p.k1, t), k1);
-    unpack<BF16>(ld(p.ki, t), ki);
-    unpack<BF16>(ld(p.v1, t), v1);
-    unpack<BF16>(ld(p.vi, t), vi);
+    gk[u] = ld(p.gk, p.t0 + t);
+    gv[u] = ld(p.gv, p.t0 + t);
+    k1[u] = ld(p.k1, t);
+    ki[u] = ld(p.ki, t);
+    v1[u] = ld(p.v1, t);
+    vi[u] = ld(p.vi, t);
+    auto gp = [&](const View4& v) {
+      return reinterpret_cast<f32x4*>(static_cast<char*>(const_cast<void*>(v.ptr)) + off(v, b, h, t) * 4) + c;
+    };
+    dk1p[u] = gp(p.dk1);
+    dv1p[u] = gp(p.dv1);
+    dkip[u] = gp(p.dki);
+    dvip[u] = gp(p.dvi);
+    a1[u] = __builtin_nontemporal_load(dk1p[u]);
+    b1[u] = __builtin_nontemporal_load(dv1p[u]);
+  }
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      sk1 = __builtin_fmaf(gk[e], k1[e], sk1);
-      ski = __builtin_fmaf(gk[e], ki[e], ski);
-      sv1 = __builtin_fmaf(gv[e], v1[e], sv1);
-      svi = __builtin_fmaf(gv[e], vi[e], svi);
-    }
-    // fp32 gradients: E elements = E/4 vectors of 4 floats
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const f32x4 g = SV::unpack(gk[u]), h = SV::unpack(gv[u]);
+    const f32x4 x1 = SV::unpack(k1[u]), xi = SV::unpack(ki[u]), y1 = SV::unpack(v1[u]), yi = SV::unpack(vi[u]);
+    f32x4 ak, bv;
 #pragma unroll
-    for (int q = 0; q < E / 4; ++q) {
-      f32x4* dk1 = reinterpret_cast<f32x4*>(const_cast<char*>(elem(p.dk1, b, h, t, 4))) + c * (E / 4) + q;
-      f32x4* dki = reinterpret_cast<f32x4*>(const_cast<char*>(elem(p.dki, b, h, t, 4))) + c * (E / 4) + q;
-      f32x4* dv1 = reinterpret_cast<f32x4*>(const_cast<char*>(elem(p.dv1, b, h, t, 4))) + c * (E / 4) + q;
-      f32x4* dvi = reinterpret_cast<f32x4*>(const_cast<char*>(elem(p.dvi, b, h, t, 4))) + c * (E / 4) + q;
-      f32x4 a1 = *dk1, b1 = *dv1, ak, bv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a1[e] = __builtin_fmaf(p.cK1, gk[4 * q + e], a1[e]);
-        b1[e] = __builtin_fmaf(p.cV1, gv[4 * q + e], b1[e]);
-        ak[e] = p.cK2 * gk[4 * q + e];
-        bv[e] = p.cV2 * gv[4 * q + e];
+    for (int e = 0; e < 4; ++e) {
+      if (live[u]) {
+        sk1 = __builtin_fmaf(g[e], x1[e], sk1);
+        ski = __builtin_fmaf(g[e], xi[e], ski);
+        sv1 = __builtin_fmaf(h[e], y1[e], sv1);
+        svi = __builtin_fmaf(h[e], yi[e], svi);
       }
-      *dk1 = a1;
-      *dv1 = b1;
-      __builtin_nontemporal_store(ak, dki);
-      __builtin_nontemporal_store(bv, dvi);
+      a1[u][e] = __builtin_fmaf(p.cK1, g[e], a1[u][e]);
+      b1[u][e] = __builtin_fmaf(p.cV1, h[e], b1[u][e]);
+      ak[e] = p.cK2 * g[e];
+      bv[e] = p.cV2 * h[e];
+    }
+    if (live[u]) {
+      __builtin_nontemporal_store(a1[u], dk1p[u]);
+      __builtin_nontemporal_store(b1[u], dv1p[u]);
+      __builtin_nontemporal_store(ak, dkip[u]);
+      __builtin_nontemporal_store(bv, dvip[u]);
     }
   }
   // workgroup sums of the four dot products
   __shared__ float red[kThreads / 64][4];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    sk1 += __shfl_xor(sk1, off);
-    ski += __shfl_xor(ski, off);
-    sv1 += __shfl_xor(sv1, off);
-    svi += __shfl_xor(svi, off);
+  for (int o = 32; o >= 1; o >>= 1) {
+    sk1 += __shfl_xor(sk1, o);
+    ski += __shfl_xor(ski, o);
+    sv1 += __shfl_xor(sv1, o);
+    svi += __shfl_xor(svi, o);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
@@ -120,35 +153,42 @@ __global__ __launch_bounds__(kThreads) void compose_backward_kernel(ComposeBackw
 }
 
 // dalpha[k] = lambda * sum over workgroups of partial[wg][k], summed in fp64 in a fixed order.
-__global__ __launch_bounds__(kThreads) void compose_backward_finish(const float* __restrict__ partial, int nblocks,
-                                                                    float lambda, float* __restrict__ dalpha) {
-  __shared__ double red[kThreads][4];
+__global__ __launch_bounds__(kFinishThreads) void compose_backward_finish(const float* __restrict__ partial,
+                                                                         int nblocks, float lambda,
+                                                                         float* __restrict__ dalpha) {
+  __shared__ double red[kFinishThreads / 64][4];
   double s[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int i = threadIdx.x; i < nblocks; i += kThreads)
+  for (int i = threadIdx.x; i < nblocks; i += kFinishThreads) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(partial + 4 * (size_t)i);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) s[k] += (double)partial[i * 4 + k];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) red[threadIdx.x][k] = s[k];
-  __syncthreads();
-  for (int stride = kThreads / 2; stride > 0; stride >>= 1) {
-    if ((int)threadIdx.x < stride)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) red[threadIdx.x][k] += red[threadIdx.x + stride][k];
-    __syncthreads();
+    for (int k = 0; k < 4; ++k) s[k] += (double)v[k];
   }
-  if (threadIdx.x < 4) dalpha[threadIdx.x] = (float)((double)lambda * red[0][threadIdx.x]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s[k] += __shfl_xor(s[k], o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red[wave][k] = s[k];
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    double t = 0.0;
+    for (int w = 0; w < kFinishThreads / 64; ++w) t += red[w][threadIdx.x];
+    dalpha[threadIdx.x] = (float)((double)lambda * t);
+  }
 }
 
 }  // namespace
 
 int compose_backward_blocks(const ComposeBackwardParams& p, bool bf16) {
-  const uint64_t cpr = (uint64_t)p.D * (bf16 ? 2 : 4) / 16;
-  const uint64_t total = (uint64_t)p.B * p.n * p.Hkv * cpr;
-  return (int)((total + kThreads - 1) / kThreads);
+  (void)bf16;
+  const uint64_t total = (uint64_t)p.B * p.n * p.Hkv * (p.D / 4);
+  return (int)((total + kThreads * kVecPerThread - 1) / (kThreads * kVecPerThread));
 }
 
 hipError_t launch_compose_backward(const ComposeBackwardParams& p, bool bf16, float* partial, hipStream_t stream) {
-  const uint32_t cpr = (uint32_t)(p.D * (bf16 ? 2 : 4) / 16);
+  const uint32_t cpr = (uint32_t)(p.D / 4);
   const uint32_t total = (uint32_t)((uint64_t)p.B * p.n * p.Hkv * cpr);
   const int nb = compose_backward_blocks(p, bf16);
   if (bf16)
@@ -157,7 +197,7 @@ hipError_t launch_compose_backward(const ComposeBackwardParams& p, bool bf16, fl
     compose_backward_kernel<false><<<nb, kThreads, 0, stream>>>(p, cpr, total, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  compose_backward_finish<<<1, kThreads, 0, stream>>>(partial, nb, p.lambda, p.dalpha);
+  compose_backward_finish<<<1, kFinishThreads, 0, stream>>>(partial, nb, p.lambda, p.dalpha);
   return hipGetLastError();
 }
 

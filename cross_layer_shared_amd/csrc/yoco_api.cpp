@@ -240,8 +240,8 @@ yoco_status yoco_compose_kv_backward(yoco_tensor4 gk, yoco_tensor4 gv, int t0, y
     return fail(YOCO_ERR_UNSUPPORTED, "compose backward needs D*elemsize a multiple of 16 bytes and D <= 1024");
   if (!isfinite(lambda) || !isfinite(aK1) || !isfinite(aK2) || !isfinite(aV1) || !isfinite(aV2))
     return fail(YOCO_ERR_INVALID_ARG, "lambda and the weights must be finite");
-  if ((uint64_t)B * n * Hkv * (D * es / 16) >= (1ull << 31))
-    return fail(YOCO_ERR_UNSUPPORTED, "compose backward call too large (more than 2^31 16-byte vectors)");
+  if ((uint64_t)B * n * Hkv * (D / 4) >= (1ull << 31))
+    return fail(YOCO_ERR_UNSUPPORTED, "compose backward call too large (more than 2^31 four-element vectors)");
   yoco_status st;
   const char* in_names[6] = {"gk", "gv", "k1", "ki", "v1", "vi"};
   const yoco_tensor4* ins[6] = {&gk, &gv, &k1, &ki, &v1, &vi};

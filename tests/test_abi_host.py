@@ -185,7 +185,9 @@ def test_compose_backward_rejects(lib):
     assert call(g=[Tensor4(src[0].ptr, 256 * 8 * 128, 128, 8 * 128, 256)] + g32[1:]) == INVALID   # output over input
     assert call(gk=t4(BASE + (4 << 24), rows=100)) == INVALID
     assert call(lam=float("inf")) == INVALID
-    assert Y.yoco_compose_backward_workspace_size(1, 256, 8, 128, BF16) == ((256 * 8 * 16 + 255) // 256) * 16
+    # one fp32 partial per weight per workgroup of 256 threads x 4 four-element vectors
+    assert Y.yoco_compose_backward_workspace_size(1, 256, 8, 128, BF16) == ((256 * 8 * 32 + 1023) // 1024) * 16
+    assert Y.yoco_compose_backward_workspace_size(1, 3, 1, 64, F32) == 16
 
 
 def prefill(lib, **kw):

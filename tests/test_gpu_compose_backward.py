@@ -69,3 +69,10 @@ def test_backward_identity_init():
 def test_backward_full_prefill_layer():
     """One self-decoder layer of the 32K-token workload: [1, 32768, 8, 128] bf16."""
     _case(S.PREFILL_CHUNKED, 3, 0, S.PREFILL_CHUNKED.T, S.alphas(S.PREFILL_CHUNKED.seed, 3))
+
+
+@pytest.mark.parametrize("dtype,D,n", [("f32", 64, 1), ("bf16", 64, 3), ("bf16", 128, 1)])
+def test_backward_single_rows(dtype, D, n):
+    """Fewer positions than one workgroup covers: most threads have no element."""
+    w = S.Workload("bwd_tiny", 67 + n, B=1, T=n, Hq=2, Hkv=1, D=D, dtype=dtype)
+    _case(w, 5, 2, n + 4, S.alphas(w.seed, 5))
