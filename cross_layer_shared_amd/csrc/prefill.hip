@@ -23,6 +23,13 @@
 // k-step 8 consecutive keys: two transposing reads of 4 keys each.
 // Probabilities are rounded to bf16 for the PV product; the normaliser sums
 // the same fp32 values.
+//
+// Every workgroup of one (sequence, kv head) streams the same K and V tiles,
+// so the tiles are loaded through the L2 (temporal loads), and the 1-D grid is
+// mapped so that all workgroups of one (sequence, head group) run on the same
+// XCD (workgroups are dealt round-robin to the 8 XCDs, each with its own L2):
+// the workgroups resident on an XCD walk one kv head's tiles nearly in step
+// and share each fetch.
 
 #include <math.h>
 
@@ -84,11 +91,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 5;          // lane half
   const int j = lane & 31;          // query column of this lane
-  const int n_qgroups = gridDim.x;
-  const int qg = n_qgroups - 1 - (int)blockIdx.x;   // heaviest (latest) query blocks first
-  const int h = blockIdx.y * HPW + (wave % HPW);
-  const int g = (blockIdx.y * HPW) / (p.Hq / p.Hkv);
-  const int b = blockIdx.z;
+  const int ngrp = p.Hq / HPW;
+  const int npair = ngrp * p.B;
+  const int n_qgroups = (int)gridDim.x / npair;
+  int pair, qlin;
+  {
+    const int L = blockIdx.x;
+    if (npair % 8 == 0) {   // workgroup L runs on XCD L % 8: keep each (b, head group) on one XCD
+      const int x = L % 8, i = L / 8, ppx = npair / 8;
+      pair = x + 8 * (i % ppx);
+      qlin = i / ppx;
+    } else {
+      pair = L % npair;
+      qlin = L / npair;
+    }
+  }
+  const int qg = n_qgroups - 1 - qlin;   // heaviest (latest) query blocks first
+  const int hgrp = pair % ngrp;
+  const int h = hgrp * HPW + (wave % HPW);
+  const int g = (hgrp * HPW) / (p.Hq / p.Hkv);
+  const int b = pair / ngrp;
   const int c_wg = qg * (WQ * kQB);                 // first chunk row of the workgroup
   const int c_w = c_wg + (wave / HPW) * kQB;        // first chunk row of this wavefront
   const int c_hi = min(c_wg + WQ * kQB, p.C);       // workgroup rows end
@@ -119,15 +141,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const char* vp = vbase + row0 * vst;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + i * kst));
-        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + i * vst));
+        kreg[i] = *reinterpret_cast<const u32x4*>(kp + i * kst);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vp + i * vst);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = min(row0 + i, kv_len - 1);
-        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + row * kst));
-        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + row * vst));
+        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + row * kst);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + row * vst);
       }
     }
   };
@@ -290,7 +312,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 template <int HPW>
 hipError_t launch_hpw(const PrefillParams& p, hipStream_t s) {
   constexpr int WQ = kWaves / HPW;
-  dim3 grid((p.C + WQ * kQB - 1) / (WQ * kQB), p.Hq / HPW, p.B);
+  dim3 grid(((p.C + WQ * kQB - 1) / (WQ * kQB)) * (p.Hq / HPW) * p.B);
   if (p.out_bf16)
     prefill_kernel<HPW, true><<<grid, kThreads, 0, s>>>(p);
   else
