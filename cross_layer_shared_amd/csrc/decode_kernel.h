@@ -87,6 +87,33 @@ struct Layout {
   typedef typename DW<kNDW>::type vec;
 };
 
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros (dword 3 = 32-bit data format, unswizzled, as gfx950 expects).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kLoadNT = 2;   // cache policy: nontemporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// N dwords (N = 2, 4 or 8) at byte offset off of a buffer, nontemporal.
+template <int N>
+__device__ __forceinline__ typename DW<N>::type buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (N == 2) {
+    return __builtin_bit_cast(typename DW<2>::type, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNT));
+  } else if constexpr (N == 4) {
+    return __builtin_bit_cast(typename DW<4>::type, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadNT));
+  } else {
+    static_assert(N == 8, "row slices are 2, 4 or 8 dwords");
+    const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadNT);
+    const i32x4 c = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off + 16, 0, kLoadNT);
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const i32x8 v = __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename DW<8>::type, v);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ uint32_t dw_at(const typename DW<N>::type& v, int i) {
   if constexpr (N == 1) {
@@ -264,18 +291,29 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
                       s * EPL * L::kES;
   const int64_t kst = p.k.st * L::kES, vst = p.v.st * L::kES;
 
+  // The split's rows stream through buffer resources over rows [0, te) of
+  // (b, g): a lane's address is one 32-bit offset (the host checks that a
+  // head's rows span less than 2 GiB), and rows at or past te read as zeros,
+  // so the last block needs no clamping (its scores are masked below).
+  auto head_rows = [&](const View4& t, int64_t st_b) {
+    return rows_rsrc(static_cast<const char*>(t.ptr) + ((int64_t)b * t.sb + (int64_t)g * t.sh) * L::kES,
+                     te > 0 ? (uint32_t)te * (uint32_t)st_b : 0u);
+  };
+  const auto rk = head_rows(p.k, kst), rv = head_rows(p.v, vst);
+  const uint32_t lane_k = (uint32_t)j * (uint32_t)kst + s * EPL * L::kES;
+  const uint32_t lane_v = (uint32_t)j * (uint32_t)vst + s * EPL * L::kES;
+
   // Compose on read: layer 1's rows are read as well and K', V' are formed per
   // row with the compose kernel's arithmetic (two KV sets read instead of one).
-  const char* k1base = nullptr;
-  const char* v1base = nullptr;
-  int64_t k1st = 0, v1st = 0;
+  __amdgpu_buffer_rsrc_t rk1 = rk, rv1 = rv;
+  uint32_t k1st = 0, v1st = 0, lane_k1 = 0, lane_v1 = 0;
   if constexpr (COR) {
-    k1base = static_cast<const char*>(p.k1.ptr) + ((int64_t)b * p.k1.sb + (int64_t)g * p.k1.sh) * L::kES +
-             s * EPL * L::kES;
-    v1base = static_cast<const char*>(p.v1.ptr) + ((int64_t)b * p.v1.sb + (int64_t)g * p.v1.sh) * L::kES +
-             s * EPL * L::kES;
-    k1st = p.k1.st * L::kES;
-    v1st = p.v1.st * L::kES;
+    k1st = (uint32_t)(p.k1.st * L::kES);
+    v1st = (uint32_t)(p.v1.st * L::kES);
+    rk1 = head_rows(p.k1, k1st);
+    rv1 = head_rows(p.v1, v1st);
+    lane_k1 = (uint32_t)j * k1st + s * EPL * L::kES;
+    lane_v1 = (uint32_t)j * v1st + s * EPL * L::kES;
   }
   auto compose_vec = [&](const vec& x1, const vec& xi, float c1, float c2, int terms) {
     vec out;
@@ -307,22 +345,15 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
 
   auto load = [&](int base, vec (&kr)[U], vec (&vr)[U]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int row = min(base + 4 * u + j, te - 1);
-      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(kbase + row * kst));
-    }
+    for (int u = 0; u < U; ++u) kr[u] = buffer_load<NDW>(rk, lane_k + (uint32_t)(base + 4 * u) * (uint32_t)kst);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int row = min(base + 4 * u + j, te - 1);
-      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(vbase + row * vst));
-    }
+    for (int u = 0; u < U; ++u) vr[u] = buffer_load<NDW>(rv, lane_v + (uint32_t)(base + 4 * u) * (uint32_t)vst);
     if constexpr (COR) {
       vec k1r[U], v1r[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        int row = min(base + 4 * u + j, te - 1);
-        k1r[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(k1base + row * k1st));
-        v1r[u] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(v1base + row * v1st));
+        k1r[u] = buffer_load<NDW>(rk1, lane_k1 + (uint32_t)(base + 4 * u) * k1st);
+        v1r[u] = buffer_load<NDW>(rv1, lane_v1 + (uint32_t)(base + 4 * u) * v1st);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

@@ -64,6 +64,14 @@ yoco_status check_tensor(const char* name, const yoco_tensor4& t, int64_t rows_n
   return YOCO_OK;
 }
 
+// The decode kernels address one (sequence, head)'s rows with 32-bit byte
+// offsets: rows [0, T) plus one block of overrun must span less than 2 GiB.
+yoco_status check_head_span(const char* name, const yoco_tensor4& t, int64_t T, size_t es) {
+  if ((T + 64) * t.stride_t * (int64_t)es >= (int64_t)1 << 31)
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: the rows of one (sequence, head) span 2 GiB or more", name);
+  return YOCO_OK;
+}
+
 yoco::View4 view(const yoco_tensor4& t) { return {t.ptr, t.stride_b, t.stride_h, t.stride_t}; }
 
 yoco_status launched(hipError_t e, const char* what) {
@@ -99,8 +107,8 @@ yoco_status check_decode(const void* q, const yoco_tensor4& k, const yoco_tensor
   yoco_status st;
   if ((st = check_tensor("k_cache", k, T, es)) != YOCO_OK) return st;
   if ((st = check_tensor("v_cache", v, T, es)) != YOCO_OK) return st;
-  if ((int64_t)T * k.stride_t > (int64_t)INT32_MAX * 4 || (int64_t)T > INT32_MAX / 2)
-    return fail(YOCO_ERR_UNSUPPORTED, "cache too long");
+  if ((st = check_head_span("k_cache", k, T, es)) != YOCO_OK) return st;
+  if ((st = check_head_span("v_cache", v, T, es)) != YOCO_OK) return st;
   return YOCO_OK;
 }
 
@@ -416,6 +424,8 @@ yoco_status yoco_cross_attn_decode_compose_on_read(const void* q, yoco_tensor4 k
   const size_t es = esize(kv_dtype);
   if ((st = check_tensor("k1_cache", k1_cache, T, es)) != YOCO_OK) return st;
   if ((st = check_tensor("v1_cache", v1_cache, T, es)) != YOCO_OK) return st;
+  if ((st = check_head_span("k1_cache", k1_cache, T, es)) != YOCO_OK) return st;
+  if ((st = check_head_span("v1_cache", v1_cache, T, es)) != YOCO_OK) return st;
   if (!isfinite(lambda) || !isfinite(aK1) || !isfinite(aK2) || !isfinite(aV1) || !isfinite(aV2))
     return fail(YOCO_ERR_INVALID_ARG, "lambda and the weights must be finite");
   if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");

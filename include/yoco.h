@@ -180,6 +180,10 @@ size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_
  *   num_splits 0 = automatic; otherwise the split count S >= 1.
  *   kv_dtype   YOCO_F32 or YOCO_BF16; D in {64, 128}; Hq a multiple of Hkv,
  *              Hq / Hkv in {1, 2, 4, 8, 16}.
+ * The rows of one (sequence, kv head) are addressed with 32-bit offsets:
+ * (T + 64) * stride_t * element size must stay below 2 GiB for each cache
+ * (YOCO_ERR_UNSUPPORTED otherwise; a head-major 1M-token bf16 D = 128 cache
+ * spans 256 MiB).
  */
 yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
                                    const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D,

@@ -106,6 +106,10 @@ def decode(lib, **kw):
     (dict(T=5000), INVALID), (dict(S=-1), INVALID), (dict(S=5000), INVALID),
     (dict(ws=None), WORKSPACE), (dict(wsb=1000), WORKSPACE), (dict(ws=BASE + 8), ALIGN),
     (dict(sl=BASE + 2), ALIGN), (dict(scale=float("inf")), INVALID),
+    # one head's rows must span less than 2 GiB (32-bit row offsets)
+    (dict(k=t4(BASE + (1 << 28), rows=1 << 23, sb=0, sh=0, st=128), v=t4(BASE + (1 << 40), rows=1 << 23, sb=0, sh=0),
+          T=1 << 23, B=1, S=1), UNSUPPORTED),
+    (dict(v=t4(BASE + (2 << 28), rows=4096, sb=0, sh=0, st=128 * 4096)), UNSUPPORTED),
 ])
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
