@@ -408,9 +408,10 @@ def counter_traffic():
     if not os.path.exists(rec_path):
         return None
     rec = json.load(open(rec_path))
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
-        return None
+    for rel, digest in rec["sources"].items():
+        src = os.path.join(ROOT, rel)
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != digest:
+            return None
     return 1024.0 * (rec["fetch_kib_per_launch"] * rec["fetch_scale"] + rec["write_kib_per_launch"] * rec["write_scale"])
 
 
