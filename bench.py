@@ -8,10 +8,13 @@ decode attention (split pass + log-sum-exp merge) over that same cache.
 once per layer) per second of step time.
 
 Further legs, reported in the same JSON line: the compose of the 32K-token
-prefill workload's 15 composed self-decoder layers (GB/s), the causal chunked
-prefill over that workload's global cache (TFLOP/s over unmasked pairs), the
-two long-context decodes (131K tokens x 4 sequences; 1M tokens), cold-cache
-decode timings, and a plain device copy as the achievable-bandwidth reference.
+prefill workload's 15 composed self-decoder layers (GB/s) and the backward of
+one such layer, the causal chunked prefill over that workload's global cache
+(TFLOP/s over unmasked pairs), that prefill's cache path with and without the
+early exit, the compose-on-read comparator, one self-decoder decode step over
+16 layers (fused append against compose-then-decode), the two long-context
+decodes (131K tokens x 4 sequences; 1M tokens), cold-cache decode timings, and
+a plain device copy as the achievable-bandwidth reference.
 
 cpu_baseline: the fp64 oracle (as it stands) timed on the host cores over a
 bounded sample of the headline workload (a few of its decode layers).
