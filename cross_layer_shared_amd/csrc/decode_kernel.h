@@ -188,9 +188,9 @@ __device__ __forceinline__ float load_agent(const float* p) {
 }
 
 // LSE merge of S split partials for G consecutive heads (rows bh0 .. bh0+G-1 of
-// [B*Hq]); the heads are spread over the NW wavefronts. Per head: M = max_s lse_s
-// (lanes stride over the splits), then the weighted sum over the splits in
-// batches of 8 whose loads are all issued before they are used.
+// [B*Hq]); the heads are spread over the NW wavefronts. Per head, the splits are
+// taken in batches of 8 whose loads are all issued before they are used, with a
+// running maximum (online rescaling) so that no separate pass finds the maximum.
 template <int D, int G, int NW, bool AGENT>
 __device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                                              int S, int bh0, float* __restrict__ out, float* __restrict__ lse) {
@@ -200,11 +200,9 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, c
   auto ld = [](const float* p) { return AGENT ? load_agent(p) : *p; };
   for (int hh = wave; hh < G; hh += NW) {
     const size_t r0 = (size_t)(bh0 + hh) * S;
-    float M = -INFINITY;
-    for (int i = lane; i < S; i += 64) M = fmaxf(M, ld(&part_lse[r0 + i]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.f, o[PER];
+    // one pass: the running maximum M rescales the sums when a batch raises it,
+    // so a split count up to BATCH costs a single round of loads
+    float M = -INFINITY, L = 0.f, o[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) o[k] = 0.f;
     for (int i0 = 0; i0 < S; i0 += BATCH) {
@@ -216,14 +214,27 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, c
 #pragma unroll
         for (int k = 0; k < PER; ++k) ov[u][k] = ld(&part_o[(r0 + i) * D + lane + 64 * k]);
       }
+      // empty splits (lse = -inf) and the clamped tail of the last batch weigh 0
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (i0 + u >= S) li[u] = -INFINITY;
+      float mb = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) mb = fmaxf(mb, li[u]);
+      if (mb == -INFINITY) continue;   // the same for every lane: all lanes read the same lse values
+      const float Mn = fmaxf(M, mb);
+      const float keep = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+      L *= keep;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] *= keep;
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        // empty splits (lse = -inf) and the clamped tail of the last batch weigh 0
-        const float w = (i0 + u >= S || li[u] == -INFINITY) ? 0.f : __expf(li[u] - M);
+        const float w = (li[u] == -INFINITY) ? 0.f : __expf(li[u] - Mn);
         L += w;
 #pragma unroll
         for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(w, ov[u][k], o[k]);
       }
+      M = Mn;
     }
     const float inv = 1.0f / L;
 #pragma unroll
