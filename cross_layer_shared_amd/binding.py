@@ -130,6 +130,15 @@ def _as_t4(x) -> Tensor4:
     return x if isinstance(x, Tensor4) else head_major(x)
 
 
+def _heads(cache, Hkv: int | None) -> int:
+    """KV head count: given explicitly, or axis 1 of a head-major [B, Hkv, T, D] tensor."""
+    if Hkv is not None:
+        return int(Hkv)
+    if isinstance(cache, Tensor4):
+        raise ValueError("pass Hkv with a Tensor4 cache view")
+    return cache.shape[1]
+
+
 # ----------------------------------------------------------------- entry points
 
 def yoco_compose_kv(k1, ki, v1, vi, k_cache, v_cache, t0: int, alpha, lam: float = 35.0, stream=None,
@@ -190,13 +199,13 @@ def decode_workspace(B, T, Hq, Hkv, D, num_splits=0, device="cuda") -> torch.Ten
 
 def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T: int | None = None,
                            num_splits: int = 0, workspace: torch.Tensor | None = None, scale: float = 0.0,
-                           stream=None) -> None:
+                           stream=None, Hkv: int | None = None) -> None:
     """q [B, Hq, D]; caches [B, Hkv, T, D]; out [B, Hq, D] fp32; lse [B, Hq] fp32."""
     lib = load_library()
     _need_contiguous(q=q, out=out, lse=lse, seq_lens=seq_lens)
     B, Hq, D = q.shape
     kc, vc = _as_t4(k_cache), _as_t4(v_cache)
-    Hkv = k_cache.shape[1] if isinstance(k_cache, torch.Tensor) else None
+    Hkv = _heads(k_cache, Hkv)
     T = kc.rows if T is None else T
     if workspace is None:
         workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
@@ -209,13 +218,13 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T:
 def yoco_cross_attn_decode_compose_on_read(q, k1_cache, ki_cache, v1_cache, vi_cache, alpha, out, lse=None,
                                            lam: float = 35.0, seq_lens=None, T: int | None = None,
                                            num_splits: int = 0, workspace: torch.Tensor | None = None,
-                                           scale: float = 0.0, stream=None) -> None:
+                                           scale: float = 0.0, stream=None, Hkv: int | None = None) -> None:
     """Decode over raw caches of layer 1 and layer i, composing K', V' per row on read."""
     lib = load_library()
     _need_contiguous(q=q, out=out, lse=lse, seq_lens=seq_lens)
     B, Hq, D = q.shape
     k1, ki, v1, vi = (_as_t4(x) for x in (k1_cache, ki_cache, v1_cache, vi_cache))
-    Hkv = ki_cache.shape[1]
+    Hkv = _heads(ki_cache, Hkv)
     T = ki.rows if T is None else T
     if workspace is None:
         workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
@@ -241,7 +250,8 @@ def _source_t4(x) -> Tensor4:
 
 def yoco_self_attn_decode(q, k1_new, ki_new, v1_new, vi_new, k_cache, v_cache, alpha, out, lse=None,
                           lam: float = 35.0, seq_lens=None, T: int | None = None, num_splits: int = 0,
-                          workspace: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> None:
+                          workspace: torch.Tensor | None = None, scale: float = 0.0, stream=None,
+                          Hkv: int | None = None) -> None:
     """Self-decoder decode step of layer i: compose the new token's K', V' (sources [B, Hkv, D]
     one-token tensors, [B, Hkv, T, D] caches read at row seq_len-1, or Tensor4), write them at
     row seq_len-1 of k_cache, v_cache [B, Hkv, T, D] and attend over rows [0, seq_len)."""
@@ -250,7 +260,7 @@ def yoco_self_attn_decode(q, k1_new, ki_new, v1_new, vi_new, k_cache, v_cache, a
     B, Hq, D = q.shape
     srcs = [_source_t4(x) for x in (k1_new, ki_new, v1_new, vi_new)]
     kc, vc = _as_t4(k_cache), _as_t4(v_cache)
-    Hkv = k_cache.shape[1]
+    Hkv = _heads(k_cache, Hkv)
     T = kc.rows if T is None else T
     if workspace is None:
         workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
@@ -262,12 +272,13 @@ def yoco_self_attn_decode(q, k1_new, ki_new, v1_new, vi_new, k_cache, v_cache, a
 
 
 def yoco_cross_attn_decode_partial(q, k_cache, v_cache, workspace, num_splits: int, seq_lens=None,
-                                   T: int | None = None, scale: float = 0.0, stream=None) -> None:
+                                   T: int | None = None, scale: float = 0.0, stream=None,
+                                   Hkv: int | None = None) -> None:
     lib = load_library()
     _need_contiguous(q=q, workspace=workspace, seq_lens=seq_lens)
     B, Hq, D = q.shape
     kc, vc = _as_t4(k_cache), _as_t4(v_cache)
-    Hkv = k_cache.shape[1]
+    Hkv = _heads(k_cache, Hkv)
     T = kc.rows if T is None else T
     _check(lib.yoco_cross_attn_decode_partial(q.data_ptr(), kc, vc, _ptr(seq_lens), B, T, Hq, Hkv, D, float(scale),
                                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -282,7 +293,8 @@ def yoco_decode_merge(workspace, B: int, Hq: int, Hkv: int, D: int, num_splits: 
                                  int(num_splits), out.data_ptr(), _ptr(lse), _stream(stream)))
 
 
-def yoco_cross_attn_prefill(q, k_cache, v_cache, p0: int, out, lse=None, scale: float = 0.0, stream=None) -> None:
+def yoco_cross_attn_prefill(q, k_cache, v_cache, p0: int, out, lse=None, scale: float = 0.0, stream=None,
+                            Hkv: int | None = None) -> None:
     """q [B, C, Hq, D] bf16; caches [B, Hkv, Tcap, D] bf16; out [B, C, Hq, D] fp32 or bf16; lse [B, Hq, C]."""
     lib = load_library()
     B, C, Hq, D = q.shape
@@ -290,7 +302,7 @@ def yoco_cross_attn_prefill(q, k_cache, v_cache, p0: int, out, lse=None, scale: 
     # but not across sequences when B > 1; the kernel needs [B, C, Hq, D] dense
     _need_contiguous(q=q, out=out, lse=lse)
     kc, vc = _as_t4(k_cache), _as_t4(v_cache)
-    Hkv = k_cache.shape[1]
+    Hkv = _heads(k_cache, Hkv)
     _check(lib.yoco_cross_attn_prefill(q.data_ptr(), kc, vc, B, C, int(p0), Hq, Hkv, D, float(scale), out.data_ptr(),
                                        _dtype_code(out), _ptr(lse), _dtype_code(q), _stream(stream)))
 
