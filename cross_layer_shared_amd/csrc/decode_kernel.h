@@ -602,18 +602,32 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __r
   merge_splits<D, G, kWaves, false>(part_o, part_lse, S, blockIdx.x * G, out, lse);
 }
 
+// One launch. Two register sets of rows (prefetch) only where a set is small:
+// a set holds 2 * (16 / G) row slices of NDW dwords (more with compose on
+// read), and the small-G or fp32 D = 128 shapes would spill with two. The
+// wavefront count, and with it the order of every sum, stays as chosen.
+template <bool BF16, int D, int G, int NW, bool PF, int MODE>
+hipError_t launch_one(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  constexpr int set_regs = (MODE == kComposeOnRead ? 4 : 2) * (16 / G) * Layout<BF16, D>::kNDW;
+  if constexpr (PF && set_regs > 32) {
+    decode_split_kernel<BF16, D, G, NW, false, MODE><<<grid, 64 * NW, 0, s>>>(p);
+  } else {
+    decode_split_kernel<BF16, D, G, NW, PF, MODE><<<grid, 64 * NW, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
 template <bool BF16, int D, int NW, bool PF, int MODE>
 hipError_t launch_gc(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.num_splits, p.Hkv, p.B);
   switch (p.Hq / p.Hkv) {
-    case 1: decode_split_kernel<BF16, D, 1, NW, PF, MODE><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 2: decode_split_kernel<BF16, D, 2, NW, PF, MODE><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 4: decode_split_kernel<BF16, D, 4, NW, PF, MODE><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 8: decode_split_kernel<BF16, D, 8, NW, PF, MODE><<<grid, 64 * NW, 0, s>>>(p); break;
-    case 16: decode_split_kernel<BF16, D, 16, NW, PF, MODE><<<grid, 64 * NW, 0, s>>>(p); break;
+    case 1: return launch_one<BF16, D, 1, NW, PF, MODE>(p, grid, s);
+    case 2: return launch_one<BF16, D, 2, NW, PF, MODE>(p, grid, s);
+    case 4: return launch_one<BF16, D, 4, NW, PF, MODE>(p, grid, s);
+    case 8: return launch_one<BF16, D, 8, NW, PF, MODE>(p, grid, s);
+    case 16: return launch_one<BF16, D, 16, NW, PF, MODE>(p, grid, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <bool BF16, int D, int MODE>
