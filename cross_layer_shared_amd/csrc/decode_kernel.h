@@ -4,9 +4,11 @@
 // the cache is the middle layer's composed K'_{L/2}, V'_{L/2}; section 3:
 // decoding reads exactly one KV set per layer).
 //
-// Split pass: one workgroup (4 wavefronts) per (sequence b, kv head g,
-// split s) streams the split's rows of K' and V' exactly once. The G = Hq/Hkv
-// query heads that share kv head g are all served from the same loaded row.
+// Split pass: one workgroup (4 or 8 wavefronts) per (sequence b, kv head g,
+// split s) streams the split's rows of K' and V' exactly once, through buffer
+// resources bounded at the split's end. The G = Hq/Hkv query heads that share
+// kv head g are all served from the same loaded row. Short splits double-buffer
+// the row loads where a register set of rows is small.
 //
 // Lane layout of a wavefront: the 64 lanes form four 16-lane DPP rows
 // ("groups"); in one iteration group j holds cache rows base + 4u + j for
@@ -21,7 +23,11 @@
 // online-softmax state (running max m and sum l per head, in the log2
 // domain, and the weighted value sums of its slice); the running max only
 // rescales the value sums when some lane's maximum grew. The four groups and
-// four wavefronts merge their states once per split.
+// wavefronts merge their states once per split.
+//
+// Compose on read (the comparator that caches raw K_i, V_i): layer 1's rows are
+// loaded beside layer i's and every K', V' row is formed with the compose
+// kernel's arithmetic before use.
 //
 // Self-decoder step (append mode): the sequence's last row n - 1 is the new
 // token. The split that owns it composes the token's K'_i, V'_i from its
@@ -32,7 +38,8 @@
 // Merge: the splits' normalised outputs are combined with their log-sum-exps.
 // In the combined entry point the merge is fused: every workgroup takes a
 // ticket (atomic counter per (b, g)) after writing its partial, and the last
-// one merges the S partials of its G heads and resets the counter to zero.
+// one merges the S partials of its G heads in one pass (running maximum) and
+// resets the counter to zero.
 
 #pragma once
 
