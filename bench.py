@@ -504,7 +504,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                   "cross_layers": w.layers, "step": "compose 1 new row + 16 x decode (split-K, fused merge)"},
+                   "cross_layers": w.layers, "step": "compose 1 new row + 16 x decode (split-K, fused merge)",
+                   "seeds": {x.name: x.seed for x in S.WORKLOADS.values()}},
         "roofline": roofline,
         "headline_detail": h,
         "legs": extra,
