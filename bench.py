@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--legs", default="all", help="all | headline | comma list of: compose,prefill,long,million,copy,cor,backward,self,early_exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-units", action="store_true", help="also time the oracle on one unit of each other workload")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
     ap.add_argument("--decode-splits", type=int, default=0, help="split count of the headline decodes (0: automatic)")
     ap.add_argument("--long-splits", type=int, default=0, help="split count of the long-context decodes (0: automatic)")
@@ -449,6 +450,42 @@ def cpu_baseline(args, S):
                       f"(fp64 NumPy, {t_total:.1f} s)"}
 
 
+def cpu_units(S):
+    """The fp64 oracle on the host for one work unit of each other workload (off by
+    default: a few minutes of host time): one 32K-token compose layer, one decode
+    call of each long context, and the causal prefill on the last 32 query rows of
+    the 32K-token prompt (reported as TFLOP/s of those rows' unmasked pairs)."""
+    import oracle as O
+    res = {}
+    w = S.PREFILL_CHUNKED
+    src = S.compose_sources(w, layer=3)
+    alpha = S.alphas(w.seed, 3)
+    t0 = time.perf_counter()
+    O.compose_kv(src["k1"], src["ki"], src["v1"], src["vi"], alpha)
+    dt = time.perf_counter() - t0
+    res["compose_layer"] = {"seconds": dt, "gbs": 6 * w.B * w.T * w.Hkv * w.D * 2 / dt / 1e9}
+    del src
+    for wl in (S.DECODE_LONG, S.DECODE_MILLION):
+        k, v = S.cache_kv(wl)
+        q = S.queries(wl)
+        t0 = time.perf_counter()
+        O.decode_attention(q, k, v)
+        dt = time.perf_counter() - t0
+        res[wl.name] = {"seconds": dt, "gbs": 2 * wl.B * wl.T * wl.Hkv * wl.D * 2 / dt / 1e9}
+        del k, v
+    k, v = S.cache_kv(w)
+    q = S.queries(w, rows=w.chunk)
+    rows = list(range(w.chunk - 32, w.chunk))
+    p0 = w.T - w.chunk
+    t0 = time.perf_counter()
+    O.causal_prefill(q, k, v, p0, rows=rows)
+    dt = time.perf_counter() - t0
+    flop = 4.0 * w.B * w.Hq * w.D * sum(p0 + r + 1 for r in rows)
+    res["prefill_last_32_rows"] = {"seconds": dt, "tflops": flop / dt / 1e12,
+                                   "full_pass_seconds_at_this_rate": 8.796361457664e12 / (flop / dt)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -512,6 +549,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, S)
+        if args.cpu_units:
+            line["cpu_baseline"]["units"] = cpu_units(S)
     print(json.dumps(line))
 
 
