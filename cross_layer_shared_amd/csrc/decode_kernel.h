@@ -639,7 +639,7 @@ hipError_t launch_gc(const DecodeParams& p, hipStream_t s) {
 
 template <bool BF16, int D, int MODE>
 hipError_t launch_nw(const DecodeParams& p, hipStream_t s) {
-  if (!p.prefetch) return launch_gc<BF16, D, 4, false, MODE>(p, s);
+  if (!p.prefetch) return p.waves == 8 ? launch_gc<BF16, D, 8, false, MODE>(p, s) : launch_gc<BF16, D, 4, false, MODE>(p, s);
 #ifdef YOCO_FORCE_DECODE_WAVES
   if (p.waves == 16) return launch_gc<BF16, D, 16, true, MODE>(p, s);
 #endif

@@ -195,9 +195,9 @@ yoco_status yoco_compose_kv(yoco_tensor4 k1, yoco_tensor4 ki, yoco_tensor4 v1, y
 
 // Launch shape of the split pass. Measured on MI355X (bf16, D = 128, G = 4):
 // a launch wants about kDecodeTargetWaves wavefronts; long splits run best with
-// 4 wavefronts per workgroup and one register set (4 wavefronts per SIMD
-// resident), short splits with 8 wavefronts per workgroup and double-buffered
-// row loads, which hide the load latency that few rows per wavefront expose.
+// 8 wavefronts per workgroup and one register set, short splits with 8
+// wavefronts per workgroup (4 for the shortest) and double-buffered row loads,
+// which hide the load latency that few rows per wavefront expose.
 struct DecodeShape {
   int splits, waves;
   bool prefetch;
@@ -211,12 +211,15 @@ static DecodeShape decode_shape(int B, int T, int Hkv, int S_req) {
     int64_t want = (kDecodeTargetWaves / 4 + pairs - 1) / pairs;
     int64_t most = std::max<int64_t>(1, T / (4 * kDecodeMinRowsPerWave));
     S = (int)std::max<int64_t>(1, std::min(want, most));
-    if (decode_rows_per_split(T, S) <= kDecodeShortSplit && S >= 2) S /= 2;   // fewer, fuller splits
+    const int rps0 = decode_rows_per_split(T, S);
+    // short splits: fewer, fuller ones; long splits: 8 wavefronts per workgroup
+    // and half as many workgroups (the same wavefront count, measured faster)
+    if ((rps0 <= kDecodeShortSplit || rps0 > 2 * kDecodeShortSplit) && S >= 2) S /= 2;
   }
   const int rps = decode_rows_per_split(T, S);
   sh.splits = (int)((T + (int64_t)rps - 1) / rps);   // drop splits the rounding leaves empty
   sh.prefetch = rps <= 2 * kDecodeShortSplit;
-  sh.waves = sh.prefetch && rps >= 8 * kDecodeMinRowsPerWave ? 8 : 4;
+  sh.waves = !sh.prefetch || rps >= 8 * kDecodeMinRowsPerWave ? 8 : 4;
 #ifdef YOCO_FORCE_DECODE_WAVES
   sh.waves = YOCO_FORCE_DECODE_WAVES;
   sh.prefetch = true;

@@ -217,8 +217,8 @@ def test_prefill_rejects(lib, kw, status):
 def test_split_heuristic_and_workspace():
     # launch shapes measured best on MI355X for the three decode workloads
     assert Y.yoco_decode_num_splits(8, 4096, 32, 8, 128) == 4
-    assert Y.yoco_decode_num_splits(4, 131072, 32, 8, 128) == 16
-    assert Y.yoco_decode_num_splits(1, 1 << 20, 16, 4, 128) == 128
+    assert Y.yoco_decode_num_splits(4, 131072, 32, 8, 128) == 8
+    assert Y.yoco_decode_num_splits(1, 1 << 20, 16, 4, 128) == 64
     assert Y.yoco_decode_num_splits(1, 256, 4, 1, 64) == 1
     assert Y.yoco_decode_num_splits(0, 256, 4, 1, 64) == 0
     # [B, Hkv] u32 counters + [B, Hq, S, D] f32 + [B, Hq, S] f32, sections 16-byte aligned
