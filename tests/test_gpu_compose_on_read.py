@@ -71,3 +71,11 @@ def test_mid_context_shape():
     w = S.Workload("cor3", 2, B=8, T=4096, Hq=32, Hkv=8, D=128, dtype="bf16")
     _, _, oa, la, ob, lb = _run(w, 8, S.alphas(w.seed, 8), 0)
     assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_long_splits_bitwise(splits):
+    """Splits longer than 1024 rows: one register set, 8 wavefronts per workgroup."""
+    w = S.Workload("cor4", 97, B=2, T=3000, Hq=8, Hkv=2, D=128, dtype="bf16")
+    _, _, oa, la, ob, lb = _run(w, 4, S.alphas(w.seed, 4), splits)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)

@@ -218,3 +218,15 @@ def test_mid_context_shape():
     o_ref, lse_ref, _, _ = O.self_attn_decode(q, k, v, new, alpha, seq_lens=np.array(lens))
     _check_output(o, lse, o_ref, lse_ref, "bf16", _rounding_slack(q, o_ref, lse_ref, [(new, alpha)], "bf16"))
     _check_rows(k, v, k1, v1, new, alpha, lens, "bf16")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_long_splits(dtype, D):
+    """Splits longer than 1024 rows (one register set, 8 wavefronts per workgroup)."""
+    w, q, k, v, new, alpha = _case(2, 3000, 8, 2, D, dtype, 95 + D)
+    lens = [3000, 1800]
+    for splits in (1, 2):
+        o, lse, k1, v1 = _step(q, k, v, new, alpha, lens, splits)
+        o_ref, lse_ref, _, _ = O.self_attn_decode(q, k, v, new, alpha, seq_lens=np.array(lens))
+        _check_output(o, lse, o_ref, lse_ref, dtype, _rounding_slack(q, o_ref, lse_ref, [(new, alpha)], dtype))
+        _check_rows(k, v, k1, v1, new, alpha, lens, dtype)
