@@ -13,13 +13,22 @@
 // Lane layout of a wavefront: the 64 lanes form four 16-lane DPP rows
 // ("groups"); in one iteration group j holds cache rows base + 4u + j for
 // u < U = 16/G, lane s of the group holding elements [s*D/16, (s+1)*D/16) of
-// each row. One load instruction of the wavefront therefore reads four
-// consecutive cache rows: a contiguous 1 KiB block for a bf16 D=128 cache.
+// each row. A V load instruction of the wavefront reads four consecutive
+// cache rows (a contiguous 1 KiB block for a bf16 D=128 cache).
 //
-// Scores: each lane forms the 16 = U*G partial dot products over its slice,
-// and a transposed butterfly over the 16 lanes of the group (DPP partners
-// s^8, s^7, s^2, s^1, which span the 4 lane bits) leaves lane s holding the
-// complete score of (row u, head hh) with s = u*G + hh. Each group keeps an
+// Scores: each lane forms 16 = U*G partial dot products over its slice, and a
+// transposed butterfly over the 16 lanes of the group (DPP partners s^8, s^7,
+// s^2, s^1, which span the 4 lane bits) leaves lane s holding the complete
+// score of (row u, head hh) with s = u*G + hh. The butterfly keeps, at every
+// stage, the same half of each lane's values and sends the other half when
+// slot k of lane s holds the partial of index s ^ c(k), c(k) = k ^ (k & 4 ?
+// 3 : 0) ("XOR layout"); lane s then needs K row (s / G) ^ (c(k) / G) and
+// query head (s mod G) ^ (c(k) mod G) for slot k. The query heads are loaded
+// in that permuted order once, and the K load of row slot r fetches row
+// ((s / G) ^ r) per lane, which keeps every load segment G * D/16 elements
+// long; this is used where those segments are at least 64 bytes. Otherwise
+// every lane holds the rows in plain order and the butterfly selects which
+// half to keep and send per lane bit. Each group keeps an
 // online-softmax state (running max m and sum l per head, in the log2
 // domain, and the weighted value sums of its slice); the running max only
 // rescales the value sums when some lane's maximum grew. The four groups and
@@ -65,7 +74,8 @@ constexpr int kRowNewBcast = 0x150;   // + n: broadcast lane n of each row
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  // every control used here reads a valid lane of the same row, so no lane keeps an old value
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 // Broadcast lane n (compile-time) of each 16-lane row to the whole row.
@@ -156,6 +166,21 @@ __device__ __forceinline__ float reduce16_transposed(const float (&x)[16], int s
   float keep = b0 ? y2[1] : y2[0];
   float send = b0 ? y2[0] : y2[1];
   return keep + dpp<kQuadSwap1>(send);
+}
+
+// The same reduction in the XOR layout: slot k of lane s holds the partial of
+// value index s ^ xor_slot(k), so every stage keeps the lower half of the
+// slots and sends the upper half, with no per-lane selects.
+__device__ __host__ constexpr int xor_slot(int k) { return k ^ ((k & 4) ? 3 : 0); }
+__device__ __forceinline__ float reduce16_xor(const float (&x)[16]) {
+  float y8[8], y4[4], y2[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y8[i] = x[i] + dpp<kRowRor + 8>(x[i + 8]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y4[i] = y8[i] + dpp<kHalfMirror>(y8[i + 4]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) y2[i] = y4[i] + dpp<kQuadSwap2>(y4[i + 2]);
+  return y2[0] + dpp<kQuadSwap1>(y2[1]);
 }
 
 // All-reduce (max or sum) over the lanes of a row that share s mod G.
@@ -264,6 +289,8 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   constexpr int NDW = L::kNDW;
   constexpr int U = 16 / G;          // rows per group per iteration
   constexpr int R = 4 * U;           // rows per wavefront per iteration
+  constexpr int LG = G >= 16 ? 4 : G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0;   // log2(G)
+  constexpr bool XL = G >= 4 && G * EPL * L::kES >= 64;   // XOR layout: K segments of >= 64 bytes
 
   __shared__ float sm_acc[NW][G][D];
   __shared__ float sm_m[NW][G];
@@ -289,11 +316,13 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   const int te = min(ts + p.rows_per_split, APP ? len - 1 : len);
   const bool own_new = APP && split == (len - 1) / p.rows_per_split;
 
-  // Query slices of the G heads of this group (same dims as the lane's K slice).
+  // Query slices of the G heads of this group (same dims as the lane's K
+  // slice); in the XOR layout qv[m] holds head m ^ (s mod G).
   vec qv[G];
   const char* qbase = static_cast<const char*>(p.q) + ((size_t)(b * p.Hq + g * G) * D + s * EPL) * L::kES;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) qv[hh] = *reinterpret_cast<const vec*>(qbase + (size_t)hh * D * L::kES);
+  for (int m = 0; m < G; ++m)
+    qv[m] = *reinterpret_cast<const vec*>(qbase + (size_t)(XL ? (m ^ (s & (G - 1))) : m) * D * L::kES);
 
   float acc[G][EPL];
 #pragma unroll
@@ -319,6 +348,8 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   };
   const auto rk = head_rows(p.k, kst), rv = head_rows(p.v, vst);
   const uint32_t lane_k = (uint32_t)j * (uint32_t)kst + s * EPL * L::kES;
+  // K row slot r of the lane: row base + krow(r) + j
+  auto krow = [&](int r) { return XL ? 4 * ((s >> LG) ^ r) : 4 * r; };
   const uint32_t lane_v = (uint32_t)j * (uint32_t)vst + s * EPL * L::kES;
 
   // Compose on read: layer 1's rows are read as well and K', V' are formed per
@@ -363,14 +394,14 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
 
   auto load = [&](int base, vec (&kr)[U], vec (&vr)[U]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) kr[u] = buffer_load<NDW>(rk, lane_k + (uint32_t)(base + 4 * u) * (uint32_t)kst);
+    for (int u = 0; u < U; ++u) kr[u] = buffer_load<NDW>(rk, lane_k + (uint32_t)(base + krow(u)) * (uint32_t)kst);
 #pragma unroll
     for (int u = 0; u < U; ++u) vr[u] = buffer_load<NDW>(rv, lane_v + (uint32_t)(base + 4 * u) * (uint32_t)vst);
     if constexpr (COR) {
       vec k1r[U], v1r[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        k1r[u] = buffer_load<NDW>(rk1, lane_k1 + (uint32_t)(base + 4 * u) * k1st);
+        k1r[u] = buffer_load<NDW>(rk1, lane_k1 + (uint32_t)(base + krow(u)) * k1st);
         v1r[u] = buffer_load<NDW>(rv1, lane_v1 + (uint32_t)(base + 4 * u) * v1st);
       }
 #pragma unroll
@@ -382,27 +413,27 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   };
 
   auto rows = [&](const vec (&kr)[U], const vec (&vr)[U], int base) {
-    // Partial dot products over this lane's slice: x[u*G + hh].
+    // Partial dot products over this lane's slice: slot k pairs K row slot u
+    // with query register hh (plain layout: x[u*G + hh]).
     float x[16];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int k = 0; k < 16; ++k) {
+      const int u = XL ? (xor_slot(k) >> LG) : k / G;
+      const int hh = XL ? (xor_slot(k) & (G - 1)) : k % G;
+      float a = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float a = 0.f;
-#pragma unroll
-        for (int w = 0; w < NDW; ++w) {
-          uint32_t kw = dw_at<NDW>(kr[u], w), qw = dw_at<NDW>(qv[hh], w);
-          if constexpr (BF16) {
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw), __builtin_bit_cast(bf16x2_t, kw), a,
-                                                false);
-          } else {
-            a = __builtin_fmaf(__uint_as_float(qw), __uint_as_float(kw), a);
-          }
+      for (int w = 0; w < NDW; ++w) {
+        uint32_t kw = dw_at<NDW>(kr[u], w), qw = dw_at<NDW>(qv[hh], w);
+        if constexpr (BF16) {
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw), __builtin_bit_cast(bf16x2_t, kw), a,
+                                              false);
+        } else {
+          a = __builtin_fmaf(__uint_as_float(qw), __uint_as_float(kw), a);
         }
-        x[u * G + hh] = a;
       }
+      x[k] = a;
     }
-    float sc = reduce16_transposed(x, s) * p.scale_log2;
+    float sc = (XL ? reduce16_xor(x) : reduce16_transposed(x, s)) * p.scale_log2;
     if (base + 4 * my_u + j >= te) sc = -INFINITY;
 
     float mt = reduce_same_head<G, true>(sc);
@@ -509,9 +540,15 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
       // dot product over the 16 lanes of the group) joins the state (M, lw, acc).
       if (own_new && wave == 0) {
         float x = 0.f;
+        vec qh = qv[hh];   // this lane's slice of head hh's query
+        if constexpr (XL) {
+#pragma unroll
+          for (int m = 0; m < G; ++m)
+            if ((m ^ (s & (G - 1))) == hh) qh = qv[m];
+        }
 #pragma unroll
         for (int w2 = 0; w2 < NDW; ++w2) {
-          uint32_t kw = dw_at<NDW>(kn, w2), qw = dw_at<NDW>(qv[hh], w2);
+          uint32_t kw = dw_at<NDW>(kn, w2), qw = dw_at<NDW>(qh, w2);
           if constexpr (BF16) {
             x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw), __builtin_bit_cast(bf16x2_t, kw),
                                                 x, false);
