@@ -51,6 +51,14 @@ def test_bitwise_equal_to_compose_then_decode(dtype, D, which, splits):
     assert np.array_equal(oa, ob) and np.array_equal(la, lb)
 
 
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_group_sizes_bitwise(G, dtype, D):
+    w = S.Workload("cor_g", 85 + G + D, B=2, T=333, Hq=2 * G, Hkv=2, D=D, dtype=dtype)
+    _, _, oa, la, ob, lb = _run(w, 5, S.alphas(w.seed, 5), 3)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
 @pytest.mark.parametrize("dtype,D,tol", [("bf16", 128, 1e-2), ("f32", 64, 1e-5)])
 def test_against_oracle_over_exact_composition(dtype, D, tol):
     w = S.Workload("cor2", 90, B=2, T=1500, Hq=8, Hkv=2, D=D, dtype=dtype)

@@ -130,6 +130,19 @@ def test_against_oracle(dtype, D, splits):
     _check_rows(k, v, k1, v1, new, alpha, lens, dtype)
 
 
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_group_sizes(G, dtype, D):
+    """Every GQA group size: the new row's score is folded with the query slice
+    of its own head whatever order the lane holds the heads in."""
+    w, q, k, v, new, alpha = _case(2, 300, 2 * G, 2, D, dtype, 70 + G + D)
+    lens = [300, 129]
+    o, lse, k1, v1 = _step(q, k, v, new, alpha, lens, 3)
+    o_ref, lse_ref, _, _ = O.self_attn_decode(q, k, v, new, alpha, seq_lens=np.array(lens))
+    _check_output(o, lse, o_ref, lse_ref, dtype, _rounding_slack(q, o_ref, lse_ref, [(new, alpha)], dtype))
+    _check_rows(k, v, k1, v1, new, alpha, lens, dtype)
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
 def test_written_row_is_the_compose_kernels(dtype, D):
     """All sequences full (n = T): the fused step writes at row T-1 exactly what
