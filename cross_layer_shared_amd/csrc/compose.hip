@@ -15,7 +15,7 @@
 namespace yoco {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // measured: 512 > 256 (+4.6%) > 1024
 constexpr int kUnroll = 1;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
