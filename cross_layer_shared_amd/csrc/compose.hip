@@ -7,7 +7,10 @@
 // K and V of the same position are handled by the same thread in one launch,
 // and each thread handles one position (deeper unrolling measured slower on
 // MI355X: fewer, longer-lived waves keep less in flight); nontemporal loads
-// and stores (temporal ones measured at about half the bandwidth).
+// and stores (temporal ones measured at about half the bandwidth). A thread's
+// (b, t, h, chunk) comes from its linear index by three divisions by
+// runtime-invariant sizes, each done with one high multiply (+1-2% measured
+// over the compiler's generic 32-bit division).
 
 #include "common.h"
 #include "compose_math.h"
@@ -28,8 +31,28 @@ __device__ __forceinline__ u32x4 combine(u32x4 x1, u32x4 xi, float c1, float c2)
   return out;
 }
 
+// Unsigned division by a runtime-invariant divisor d >= 1 with one high
+// multiply (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1,
+// q = (t + ((x - t) >> 1)) >> (s - 1) with t = mulhi(x, m); s = 0 means d = 1.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+static FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return {d, (uint32_t)m, s};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
+  if (f.s == 0) return x;
+  const uint32_t t = __umulhi(x, f.m);
+  return (t + ((x - t) >> 1)) >> (f.s - 1);
+}
+
 struct Args {
   ComposeParams p;
+  FastDiv dc, dh, dn;
   uint32_t cpr;     // 16-byte chunks per row (D * elemsize / 16)
   uint32_t total;   // B * n * Hkv * cpr
   int esize;        // bytes per element
@@ -53,12 +76,13 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(Args a) {
   for (int u = 0; u < kUnroll; ++u) {
     idx[u] = base + u * kThreads;
     if (idx[u] >= a.total) continue;
-    uint32_t c = idx[u] % a.cpr;
-    uint32_t r = idx[u] / a.cpr;
-    int h = (int)(r % (uint32_t)p.Hkv);
-    r /= (uint32_t)p.Hkv;
-    int t = (int)(r % (uint32_t)p.n);
-    int b = (int)(r / (uint32_t)p.n);
+    const uint32_t r0 = fdiv(idx[u], a.dc);
+    const uint32_t c = idx[u] - r0 * a.cpr;
+    const uint32_t r1 = fdiv(r0, a.dh);
+    const int h = (int)(r0 - r1 * (uint32_t)p.Hkv);
+    const uint32_t r2 = fdiv(r1, a.dn);
+    const int t = (int)(r1 - r2 * (uint32_t)p.n);
+    const int b = (int)r2;
     if constexpr (TK & 1) k1[u] = __builtin_nontemporal_load(at(p.k1, b, h, t, c, a.esize));
     if constexpr (TK & 2) ki[u] = __builtin_nontemporal_load(at(p.ki, b, h, t, c, a.esize));
     if constexpr (TV & 1) v1[u] = __builtin_nontemporal_load(at(p.v1, b, h, t, c, a.esize));
@@ -67,12 +91,13 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(Args a) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     if (idx[u] >= a.total) continue;
-    uint32_t c = idx[u] % a.cpr;
-    uint32_t r = idx[u] / a.cpr;
-    int h = (int)(r % (uint32_t)p.Hkv);
-    r /= (uint32_t)p.Hkv;
-    int t = (int)(r % (uint32_t)p.n);
-    int b = (int)(r / (uint32_t)p.n);
+    const uint32_t r0 = fdiv(idx[u], a.dc);
+    const uint32_t c = idx[u] - r0 * a.cpr;
+    const uint32_t r1 = fdiv(r0, a.dh);
+    const int h = (int)(r0 - r1 * (uint32_t)p.Hkv);
+    const uint32_t r2 = fdiv(r1, a.dn);
+    const int t = (int)(r1 - r2 * (uint32_t)p.n);
+    const int b = (int)r2;
     u32x4 ko = combine<BF16, TK>(k1[u], ki[u], p.cK1, p.cK2);
     u32x4 vo = combine<BF16, TV>(v1[u], vi[u], p.cV1, p.cV2);
     __builtin_nontemporal_store(ko, const_cast<u32x4*>(at(p.kc, b, h, p.t0 + t, c, a.esize)));
@@ -108,6 +133,9 @@ hipError_t launch_compose(const ComposeParams& p, bool bf16, hipStream_t stream)
   a.p = p;
   a.esize = bf16 ? 2 : 4;
   a.cpr = (uint32_t)(p.D * a.esize / 16);
+  a.dc = make_fastdiv(a.cpr);
+  a.dh = make_fastdiv((uint32_t)p.Hkv);
+  a.dn = make_fastdiv((uint32_t)p.n);
   a.total = (uint32_t)((uint64_t)p.B * p.n * p.Hkv * a.cpr);
   dim3 grid((a.total + kThreads * kUnroll - 1) / (kThreads * kUnroll));
   int tk = compose_terms(p.cK1, p.cK2), tv = compose_terms(p.cV1, p.cV2);
