@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "compose_math.h"
+#include "fastdiv.h"
 
 namespace yoco {
 namespace {
@@ -58,7 +59,8 @@ __device__ __forceinline__ int64_t off(const View4& v, int b, int h, int t) {
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void compose_backward_kernel(ComposeBackwardParams p, uint32_t cpr,
-                                                                    uint32_t total, float* __restrict__ partial) {
+                                                                    uint32_t total, FastDiv dc, FastDiv dh,
+                                                                    FastDiv dn, float* __restrict__ partial) {
   using SV = Src<BF16>;
   using vec = typename SV::vec;
   float sk1 = 0.f, ski = 0.f, sv1 = 0.f, svi = 0.f;
@@ -76,12 +78,13 @@ __global__ __launch_bounds__(kThreads) void compose_backward_kernel(ComposeBackw
     const uint32_t idx = first + u * kThreads;
     live[u] = idx < total;
     const uint32_t i = live[u] ? idx : total - 1;     // clamped: loads stay in bounds, results unused
-    const uint32_t c = i % cpr;
-    uint32_t r = i / cpr;
-    const int h = (int)(r % (uint32_t)p.Hkv);
-    r /= (uint32_t)p.Hkv;
-    const int t = (int)(r % (uint32_t)p.n);
-    const int b = (int)(r / (uint32_t)p.n);
+    const uint32_t r0 = fdiv(i, dc);
+    const uint32_t c = i - r0 * cpr;
+    const uint32_t r1 = fdiv(r0, dh);
+    const int h = (int)(r0 - r1 * (uint32_t)p.Hkv);
+    const uint32_t r2 = fdiv(r1, dn);
+    const int t = (int)(r1 - r2 * (uint32_t)p.n);
+    const int b = (int)r2;
     auto ld = [&](const View4& v, int row) {
       return __builtin_nontemporal_load(reinterpret_cast<const vec*>(static_cast<const char*>(v.ptr) +
                                                                      off(v, b, h, row) * SV::kES) + c);
@@ -191,10 +194,11 @@ hipError_t launch_compose_backward(const ComposeBackwardParams& p, bool bf16, fl
   const uint32_t cpr = (uint32_t)(p.D / 4);
   const uint32_t total = (uint32_t)((uint64_t)p.B * p.n * p.Hkv * cpr);
   const int nb = compose_backward_blocks(p, bf16);
+  const FastDiv dc = make_fastdiv(cpr), dh = make_fastdiv((uint32_t)p.Hkv), dn = make_fastdiv((uint32_t)p.n);
   if (bf16)
-    compose_backward_kernel<true><<<nb, kThreads, 0, stream>>>(p, cpr, total, partial);
+    compose_backward_kernel<true><<<nb, kThreads, 0, stream>>>(p, cpr, total, dc, dh, dn, partial);
   else
-    compose_backward_kernel<false><<<nb, kThreads, 0, stream>>>(p, cpr, total, partial);
+    compose_backward_kernel<false><<<nb, kThreads, 0, stream>>>(p, cpr, total, dc, dh, dn, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   compose_backward_finish<<<1, kFinishThreads, 0, stream>>>(partial, nb, p.lambda, p.dalpha);
