@@ -4,17 +4,18 @@
 // [0, p]; YOCO++ summary, section 3: prefill is compute-bound).
 //
 // Dense contraction on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
-// A workgroup of 4 wavefronts serves 4 (head, 32-query block) slots that share
-// one kv head; it streams the cache in 64-key tiles staged through LDS (two
-// stages, one barrier per tile), so that all four wavefronts read each tile
-// from LDS instead of from memory. K and V are both stored row-major; the V
-// operand of the PV product is read with the gfx950 transposing LDS read
-// (ds_read_b64_tr_b16), which hands each lane 4 consecutive keys of one dim.
+// A workgroup of 8 wavefronts serves 8 (head, 32-query block) slots that share
+// one kv head (4 heads x 2 consecutive query blocks); it streams the cache in
+// 128-key tiles staged through LDS (two stages, one barrier per tile), so that
+// all eight wavefronts read each tile from LDS instead of from memory. K and V
+// are both stored row-major; the V operand of the PV product is read with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16), which hands each lane 4
+// consecutive keys of one dim.
 //
 // Per wavefront and tile:
-//   S^T = K Q^T   (2 x 32 keys by 32 queries; D = 128 in 8 MFMA k-steps)
+//   S^T = K Q^T   (4 x 32 keys by 32 queries; D = 128 in 8 MFMA k-steps)
 //   online softmax per query column, log2 domain, fp32
-//   O^T += V^T P^T (4 x 32 dims by 32 queries; 64 keys in 4 MFMA k-steps)
+//   O^T += V^T P^T (4 x 32 dims by 32 queries; 128 keys in 8 MFMA k-steps)
 // Computing the transposed products keeps every softmax statistic of a query
 // inside one lane pair (lane j and j+32), and the S^T accumulator registers
 // become the P^T operand of the PV product without leaving the lane: the key
@@ -39,10 +40,12 @@ namespace yoco {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;             // 4 heads x 2 query blocks; one workgroup per CU
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 32;               // queries per wavefront
-constexpr int kKT = 64;               // keys per tile
+constexpr int kKT = 128;              // keys per tile (two LDS stages: 140 KiB)
+constexpr int kNB = kKT / 32;         // 32-key MFMA blocks per tile
+constexpr int kKPT = kKT / (kWaves * 4);   // keys per thread in the cooperative tile loads
 constexpr int kKPad = kD + 8;         // K tile row stride (bf16): 68 dwords, 16-lane b128 reads hit distinct banks
 constexpr int kVPad = kD + 16;        // V tile row stride (bf16): 72 dwords, 4-row tr reads hit distinct banks
 constexpr int kStage = kKT * kKPad + kKT * kVPad;   // bf16 elements per LDS stage
@@ -127,26 +130,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c);
   }
 
-  // cooperative tile loads: thread t covers dims 8*(t%16) .. +8 of keys 4*(t/16) .. +4
+  // cooperative tile loads: thread t covers dims 8*(t%16) .. +8 of keys kKPT*(t/16) .. +kKPT
   const int ld_d = 8 * (tid & 15);
-  const int ld_k = 4 * (tid >> 4);
+  const int ld_k = kKPT * (tid >> 4);
   const int64_t kst = p.k.st * 2, vst = p.v.st * 2;
   const char* kbase = static_cast<const char*>(p.k.ptr) + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh + ld_d) * 2;
   const char* vbase = static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh + ld_d) * 2;
-  u32x4 kreg[4], vreg[4];
+  u32x4 kreg[kKPT], vreg[kKPT];
   auto load_tile = [&](int t) {
     const int row0 = t * kKT + ld_k;
     if (t * kKT + kKT <= kv_len) {          // whole tile inside the cache prefix: no clamping
       const char* kp = kbase + row0 * kst;
       const char* vp = vbase + row0 * vst;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kKPT; ++i) {
         kreg[i] = *reinterpret_cast<const u32x4*>(kp + i * kst);
         vreg[i] = *reinterpret_cast<const u32x4*>(vp + i * vst);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kKPT; ++i) {
         const int row = min(row0 + i, kv_len - 1);
         kreg[i] = *reinterpret_cast<const u32x4*>(kbase + row * kst);
         vreg[i] = *reinterpret_cast<const u32x4*>(vbase + row * vst);
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __bf16* kl = lds + stage * kStage;
     __bf16* vl = kl + kKT * kKPad;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kKPT; ++i) {
       *reinterpret_cast<u32x4*>(&kl[(ld_k + i) * kKPad + ld_d]) = kreg[i];
       *reinterpret_cast<u32x4*>(&vl[(ld_k + i) * kVPad + ld_d]) = vreg[i];
     }
@@ -179,23 +182,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float l_run = 0.f;         // this lane's share of the running sum
   const float sl = p.scale_log2;
 
-  // One 64-key tile: scores, online softmax, PV, and the hand-over of the next tile.
+  // One tile of kKT keys: scores, online softmax, PV, and the hand-over of the next tile.
   auto tile = [&]<bool MASKED>(int t) {
     const int stage = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
     const __bf16* kl = lds + stage * kStage;
     const __bf16* vl = kl + kKT * kKPad;
 
-    // ---- S^T = K Q^T for 2 blocks of 32 keys (raw dot products) ----
-    f32x16 sc[2];
+    // ---- S^T = K Q^T for kNB blocks of 32 keys (raw dot products) ----
+    f32x16 sc[kNB];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < kNB; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[hb][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
+      for (int hb = 0; hb < kNB; ++hb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[32 * hb * kKPad + k_off + 16 * c]);
         sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[hb], 0, 0, 0);
       }
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // (the default schedule keeps one or two ahead; +1-2% measured).
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // 4 LDS reads
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 8 * kNB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // 1 LDS read
     }
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if constexpr (MASKED) {
       const int key0 = t * kKT;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int hb = 0; hb < kNB; ++hb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * hb + perm_key(8 * (r >> 2) + 4 * q + (r & 3));
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     float mt = -INFINITY;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < kNB; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[hb][r]);
     // the scale is positive, so the max of the scaled scores is the scaled max
@@ -241,9 +244,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     m_run = m_new;
 
     // ---- P = exp2(scale * S - m), row sums, bf16 P^T operands ----
-    bf16x8 pb[2][2];
+    bf16x8 pb[kNB][2];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < kNB; ++hb) {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         uint32_t w[4];
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < kNB; ++hb) {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         const __bf16* vk = vl + (32 * hb + 16 * hs) * kVPad + tr_off;
