@@ -1,6 +1,6 @@
 // Decode attention of the cross-decoder over the one shared cache
 // (YOCO summary, abstract and method details: every cross-decoder layer
-// reuses the global KV cache via cross-attention; YOCO++ summary, section 2:
+// attends, by cross-attention, to the one global KV cache; YOCO++ summary, section 2:
 // the cache is the middle layer's composed K'_{L/2}, V'_{L/2}; section 3:
 // decoding reads exactly one KV set per layer).
 //

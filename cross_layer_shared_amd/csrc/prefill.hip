@@ -1,6 +1,6 @@
 // Causal chunked prefill of a cross-decoder layer over the global cache
-// (YOCO summary, abstract: the model behaves like a decoder-only
-// Transformer, so the query at absolute position p attends to cache rows
+// (YOCO summary, abstract: end to end the model works as a decoder-only
+// Transformer does, so the query at absolute position p attends to cache rows
 // [0, p]; YOCO++ summary, section 3: prefill is compute-bound).
 //
 // Dense contraction on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).

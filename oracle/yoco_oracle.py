@@ -23,14 +23,14 @@ Sources:
   [YOCO]   "You Only Cache Once: Decoder-Decoder Architectures for Language
            Models" (shd-paper.top summary), abstract and method details: the
            cross-decoder reuses the global KV cache through cross-attention
-           and the whole model behaves like a decoder-only Transformer.
+           and end to end the model works as a decoder-only Transformer does.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
   * alpha holds four scalars per lower-half layer ([YOCO++] section 3 counts
     4 learnable weights per layer); lambda is a fixed constant.
   * Attention is scaled dot-product softmax attention with scale 1/sqrt(D)
-    ([YOCO]: behaves like a decoder-only Transformer).
+    ([YOCO] abstract: end to end the model works as a decoder-only Transformer does).
   * Grouped-query heads: query head h reads kv head floor(h / (Hq/Hkv)).
   * A decode query attends to every cache row [0, T), which includes the
     current token, whose composed KV the self-decoder has just written.
@@ -222,8 +222,9 @@ def self_attn_decode(q, k_cache, v_cache, new_rows: dict, alpha, seq_lens=None, 
 
 
 # ---------------------------------------------------------------------------
-# O3. Causal prefill of the cross-decoder over the global cache ([YOCO]: the
-#     model behaves like a decoder-only Transformer, so attention is causal).
+# O3. Causal prefill of the cross-decoder over the global cache ([YOCO]
+#     abstract: end to end the model works as a decoder-only Transformer does,
+#     so attention is causal).
 # ---------------------------------------------------------------------------
 
 def causal_prefill(q, k, v, p0: int, scale: float | None = None, rows=None, row_block: int = 64):

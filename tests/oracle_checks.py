@@ -10,8 +10,8 @@ a log2 lse) and require that some check fails for each.
 Sources: YOCO++ technical summary, section 2 (KV composition equations;
 key technical innovations items 2-3: lambda = 35, initialisation
 alpha_1 = 0, alpha_2 = 1/lambda); YOCO summary, abstract (cross-decoder
-reuses the global cache; behaves like a decoder-only Transformer; early exit
-leaves the output unchanged).
+reuses the global cache; end to end it works as a decoder-only Transformer
+does; early exit leaves the output unchanged).
 """
 from __future__ import annotations
 
