@@ -184,6 +184,33 @@ def test_fused_merge_reuses_one_workspace():
         _compare(host(out).astype(np.float64), host(lse).astype(np.float64), o_ref, lse_ref, "bf16")
 
 
+def test_concurrent_streams_with_their_own_workspaces():
+    """Decodes enqueued on four streams at once, each with its own workspace:
+    their fused merges count tickets independently, and every result equals the
+    same call made alone."""
+    B, Hq, Hkv, D, T, splits = 4, 16, 4, 128, 2048, 8
+    cases = [_inputs(B, T, Hq, Hkv, D, "bf16", 90 + i) for i in range(4)]
+    qs = [(dev(q), dev(k), dev(v)) for q, k, v in cases]
+    alone = []
+    for q, k, v in qs:
+        o, l = _decode(q, k, v, splits)
+        alone.append((o, l))
+    streams = [torch.cuda.Stream() for _ in qs]
+    wss = [Y.decode_workspace(B, T, Hq, Hkv, D, splits) for _ in qs]
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device="cuda") for _ in qs]
+    lses = [torch.empty((B, Hq), dtype=torch.float32, device="cuda") for _ in qs]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for (q, k, v), s, ws, o, l in zip(qs, streams, wss, outs, lses):
+            Y.yoco_cross_attn_decode(q, k, v, o, l, num_splits=splits, workspace=ws, stream=s)
+        torch.cuda.synchronize()
+        for (o_a, l_a), o, l in zip(alone, outs, lses):
+            assert np.array_equal(host(o).astype(np.float64), o_a) and np.array_equal(host(l).astype(np.float64), l_a)
+    for (q, k, v), (o_a, l_a) in zip(cases, alone):
+        o_ref, lse_ref = O.decode_attention(q, k, v)
+        _compare(o_a, l_a, o_ref, lse_ref, "bf16")
+
+
 def test_identical_keys_give_mean_value():
     q, k, v = _inputs(1, 2048, 4, 1, 128, "bf16", 44)
     k[:] = k[:, :, :1]
