@@ -96,9 +96,12 @@ def test_yoco_plus_plus_at_init_equals_yoco():
 @pytest.mark.parametrize("T", [1, 63, 65, 1000, 4097])
 @pytest.mark.parametrize("splits", [1, 2, 7, 0])
 def test_bf16_tails_and_splits(T, splits):
-    if splits > T:
-        pytest.skip("more splits than rows")
     q, k, v = _inputs(2, T, 8, 2, 128, "bf16", 20 + T)
+    if splits > T:   # more splits than rows: rejected before anything is enqueued
+        with pytest.raises(Y.YocoError) as e:
+            _decode(dev(q), dev(k), dev(v), splits)
+        assert e.value.status == 1   # YOCO_ERR_INVALID_ARG
+        return
     o, lse = _decode(dev(q), dev(k), dev(v), splits)
     o_ref, lse_ref = O.decode_attention(q, k, v)
     _compare(o, lse, o_ref, lse_ref, "bf16")
