@@ -43,11 +43,11 @@ constexpr int kD = 128;
 constexpr int kWaves = 8;             // 4 heads x 2 query blocks; one workgroup per CU
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 32;               // queries per wavefront
-constexpr int kKT = 128;              // keys per tile (two LDS stages: 140 KiB)
+constexpr int kKT = 128;              // keys per tile (two LDS stages: 148 KiB)
 constexpr int kNB = kKT / 32;         // 32-key MFMA blocks per tile
 constexpr int kKPT = kKT / (kWaves * 4);   // keys per thread in the cooperative tile loads
 constexpr int kKPad = kD + 8;         // K tile row stride (bf16): 68 dwords, 16-lane b128 reads hit distinct banks
-constexpr int kVPad = kD + 16;        // V tile row stride (bf16): 72 dwords, 4-row tr reads hit distinct banks
+constexpr int kVPad = kD + 32;        // V tile row stride (bf16): 80 dwords; no LDS bank conflicts (counters)
 constexpr int kStage = kKT * kKPad + kKT * kVPad;   // bf16 elements per LDS stage
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
