@@ -39,16 +39,23 @@
 namespace yoco {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kWaves = 8;             // 4 heads x 2 query blocks; one workgroup per CU
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 32;               // queries per wavefront
-constexpr int kKT = 128;              // keys per tile (two LDS stages: 148 KiB)
+constexpr int kKT = 128;              // keys per tile (two LDS stages: 148 KiB at D = 128)
 constexpr int kNB = kKT / 32;         // 32-key MFMA blocks per tile
-constexpr int kKPT = kKT / (kWaves * 4);   // keys per thread in the cooperative tile loads
-constexpr int kKPad = kD + 8;         // K tile row stride (bf16): 68 dwords, 16-lane b128 reads hit distinct banks
-constexpr int kVPad = kD + 32;        // V tile row stride (bf16): 80 dwords; no LDS bank conflicts (counters)
-constexpr int kStage = kKT * kKPad + kKT * kVPad;   // bf16 elements per LDS stage
+
+// Sizes that follow the head dimension (D = 64 or 128).
+template <int D>
+struct Dim {
+  static constexpr int kNQ = D / 16;            // MFMA k-steps of the score product (Q fragments)
+  static constexpr int kNDB = D / 32;           // 32-dim blocks of the output (O accumulators)
+  static constexpr int kTPR = D / 8;            // threads per tile row in the cooperative loads
+  static constexpr int kKPT = kKT / (kThreads / kTPR);   // keys per thread in the cooperative loads
+  static constexpr int kKPad = D + 8;           // K tile row stride (bf16): 16-lane b128 reads hit distinct banks
+  static constexpr int kVPad = D + 32;          // V tile row stride (bf16); no LDS bank conflicts at D = 128
+  static constexpr int kStage = kKT * kKPad + kKT * kVPad;   // bf16 elements per LDS stage
+};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -85,9 +92,11 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int HPW, bool OUT_BF16>
+template <int D, int HPW, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillParams p) {
   constexpr int WQ = kWaves / HPW;  // query blocks per workgroup
+  constexpr int kNQ = Dim<D>::kNQ, kNDB = Dim<D>::kNDB, kTPR = Dim<D>::kTPR, kKPT = Dim<D>::kKPT;
+  constexpr int kKPad = Dim<D>::kKPad, kVPad = Dim<D>::kVPad, kStage = Dim<D>::kStage;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kStage];
 
   const int tid = threadIdx.x;
@@ -123,16 +132,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // Q^T operand: lane (q, j) holds query row c_w + j, dims 16c + 8q .. +8.
   const int c_me = min(c_w + j, p.C - 1);
   const int pos = p.p0 + c_w + j;                   // absolute position of this lane's query
-  bf16x8 qf[8];
+  bf16x8 qf[kNQ];
   {
-    const __bf16* qrow = static_cast<const __bf16*>(p.q) + (((size_t)b * p.C + c_me) * p.Hq + h) * kD + 8 * q;
+    const __bf16* qrow = static_cast<const __bf16*>(p.q) + (((size_t)b * p.C + c_me) * p.Hq + h) * D + 8 * q;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c);
+    for (int c = 0; c < kNQ; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c);
   }
 
-  // cooperative tile loads: thread t covers dims 8*(t%16) .. +8 of keys kKPT*(t/16) .. +kKPT
-  const int ld_d = 8 * (tid & 15);
-  const int ld_k = kKPT * (tid >> 4);
+  // cooperative tile loads: thread t covers dims 8*(t%kTPR) .. +8 of keys kKPT*(t/kTPR) .. +kKPT
+  const int ld_d = 8 * (tid % kTPR);
+  const int ld_k = kKPT * (tid / kTPR);
   const int64_t kst = p.k.st * 2, vst = p.v.st * 2;
   const char* kbase = static_cast<const char*>(p.k.ptr) + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh + ld_d) * 2;
   const char* vbase = static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh + ld_d) * 2;
@@ -173,9 +182,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tr_off = (8 * (gq >> 1) + (sl16 >> 2)) * kVPad + 16 * (gq & 1) + 4 * (sl16 & 3);
   const int k_off = perm_key(j) * kKPad + 8 * q;
 
-  f32x16 o_acc[4];
+  f32x16 o_acc[kNDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < kNDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
   float m_run = -INFINITY;   // running max of scaled scores (log2 domain)
@@ -196,7 +205,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[hb][r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kNQ; ++c) {
 #pragma unroll
       for (int hb = 0; hb < kNB; ++hb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[32 * hb * kKPad + k_off + 16 * c]);
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // (the default schedule keeps one or two ahead; +1-2% measured).
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // 4 LDS reads
 #pragma unroll
-    for (int i = 0; i < 8 * kNB - 4; ++i) {
+    for (int i = 0; i < kNQ * kNB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // 1 LDS read
     }
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const float alpha = fast_exp2(m_run - m_use);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < kNDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[db][r] *= alpha;
     }
@@ -269,7 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int hs = 0; hs < 2; ++hs) {
         const __bf16* vk = vl + (32 * hb + 16 * hs) * kVPad + tr_off;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int db = 0; db < kNDB; ++db) {
           const s16x4 lo = read_tr16(vk + 32 * db);
           const s16x4 hi = read_tr16(vk + 32 * db + 4 * kVPad);
           typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -300,9 +309,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const float inv = 1.0f / l_tot;
   const int c_out = c_w + j;
   if (c_out < p.C) {
-    const size_t row = (((size_t)b * p.C + c_out) * p.Hq + h) * kD;
+    const size_t row = (((size_t)b * p.C + c_out) * p.Hq + h) * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < kNDB; ++db) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int d = 32 * db + 8 * rb + 4 * q;
@@ -321,25 +330,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <int HPW>
+template <int D, int HPW>
 hipError_t launch_hpw(const PrefillParams& p, hipStream_t s) {
   constexpr int WQ = kWaves / HPW;
   dim3 grid(((p.C + WQ * kQB - 1) / (WQ * kQB)) * (p.Hq / HPW) * p.B);
   if (p.out_bf16)
-    prefill_kernel<HPW, true><<<grid, kThreads, 0, s>>>(p);
+    prefill_kernel<D, HPW, true><<<grid, kThreads, 0, s>>>(p);
   else
-    prefill_kernel<HPW, false><<<grid, kThreads, 0, s>>>(p);
+    prefill_kernel<D, HPW, false><<<grid, kThreads, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dim(const PrefillParams& p, hipStream_t s) {
+  const int G = p.Hq / p.Hkv;
+  if (G >= 4) return launch_hpw<D, 4>(p, s);
+  if (G == 2) return launch_hpw<D, 2>(p, s);
+  return launch_hpw<D, 1>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  if (p.D != kD) return hipErrorInvalidValue;
-  const int G = p.Hq / p.Hkv;
-  if (G >= 4) return launch_hpw<4>(p, stream);
-  if (G == 2) return launch_hpw<2>(p, stream);
-  return launch_hpw<1>(p, stream);
+  if (p.D == 128) return launch_dim<128>(p, stream);
+  if (p.D == 64) return launch_dim<64>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace yoco

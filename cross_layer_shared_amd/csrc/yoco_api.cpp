@@ -548,7 +548,7 @@ yoco_status yoco_cross_attn_prefill(const void* q, yoco_tensor4 k_cache, yoco_te
   if (Hq % Hkv) return fail(YOCO_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return fail(YOCO_ERR_INVALID_ARG, "unknown dtype");
   if (dtype != YOCO_BF16) return fail(YOCO_ERR_UNSUPPORTED, "prefill runs on bf16 inputs only");
-  if (D != 128) return fail(YOCO_ERR_UNSUPPORTED, "prefill supports D = 128, got %d", D);
+  if (D != 64 && D != 128) return fail(YOCO_ERR_UNSUPPORTED, "prefill supports D in {64, 128}, got %d", D);
   if (!supported_group(Hq / Hkv))
     return fail(YOCO_ERR_UNSUPPORTED, "prefill supports Hq/Hkv in {1,2,4,8,16}, got %d", Hq / Hkv);
   if (!q) return fail(YOCO_ERR_INVALID_ARG, "q: null pointer");

@@ -292,7 +292,7 @@ yoco_status yoco_decode_merge(const void* workspace, size_t workspace_bytes, int
  *   k_cache, v_cache  bf16; rows [0, p0 + C) are read; p0 + C <= rows.
  *   out        [B, C, Hq, D] contiguous, out_dtype YOCO_F32 or YOCO_BF16.
  *   lse        [B, Hq, C] fp32 natural log, or NULL.
- *   dtype      must be YOCO_BF16; D = 128; Hq / Hkv in {1, 2, 4, 8, 16}.
+ *   dtype      must be YOCO_BF16; D in {64, 128}; Hq / Hkv in {1, 2, 4, 8, 16}.
  */
 yoco_status yoco_cross_attn_prefill(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache, int B,
                                     int C, int p0, int Hq, int Hkv, int D, float scale, void* out,

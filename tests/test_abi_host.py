@@ -205,7 +205,7 @@ def prefill(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(C=0), INVALID), (dict(p0=-1), INVALID), (dict(p0=4097), INVALID), (dict(Hq=33), INVALID),
-    (dict(dt=F32), UNSUPPORTED), (dict(D=64), UNSUPPORTED), (dict(Hq=8 * 32), UNSUPPORTED), (dict(odt=9), INVALID),
+    (dict(dt=F32), UNSUPPORTED), (dict(D=96), UNSUPPORTED), (dict(Hq=8 * 32), UNSUPPORTED), (dict(odt=9), INVALID),
     (dict(q=BASE + 2), ALIGN), (dict(out=None), INVALID), (dict(lse=BASE + 1), ALIGN),
     (dict(k=t4(BASE + 8, rows=8192)), ALIGN),
 ])

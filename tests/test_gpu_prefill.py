@@ -56,6 +56,24 @@ def test_small_shapes(Hq, Hkv, C, p0):
     _compare(o, lse, o_ref, lse_ref)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (32, 4), (4, 4), (32, 2)])
+@pytest.mark.parametrize("C,p0", [(1, 0), (100, 5), (300, 500)])
+def test_head_dim_64(Hq, Hkv, C, p0):
+    """D = 64 (the head size of a TinyLlama-configured model): group sizes 4, 8,
+    1 and 16, ragged chunks, several 128-key tiles."""
+    q, k, v = _inputs(2, C, Hq, Hkv, p0 + C + 7, 80 + C + p0 + Hq, D=64)
+    o, lse = _prefill(dev(q), dev(k), dev(v), p0)
+    o_ref, lse_ref = O.causal_prefill(q, k, v, p0)
+    _compare(o, lse, o_ref, lse_ref)
+
+
+def test_head_dim_64_bf16_output():
+    q, k, v = _inputs(1, 200, 8, 2, 260, 61, D=64)
+    o, lse = _prefill(dev(q), dev(k), dev(v), 50, out_dtype=torch.bfloat16)
+    o_ref, lse_ref = O.causal_prefill(q, k, v, 50)
+    _compare(o, lse, o_ref, lse_ref, out_bf16=True)
+
+
 def test_bf16_output():
     q, k, v = _inputs(1, 200, 8, 2, 260, 60)
     o, lse = _prefill(dev(q), dev(k), dev(v), 60, out_dtype=torch.bfloat16)
