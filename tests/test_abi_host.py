@@ -83,6 +83,8 @@ def compose(lib, **kw):
     # the same source buffer as the cache but at t0 > 0 is a partial overlap
     (dict(ki=t4(BASE + (4 << 24)), kc=t4(BASE + (4 << 24), rows=300), t0=16), INVALID),
     (dict(vc=t4(BASE + (4 << 24))), INVALID),
+    # 2^31 16-byte vectors in one call: beyond the kernel's 32-bit index
+    (dict(n=1 << 21, Hkv=64), UNSUPPORTED),
 ])
 def test_compose_rejects(lib, kw, status):
     assert compose(lib, **kw) == status
@@ -189,6 +191,7 @@ def test_compose_backward_rejects(lib):
     assert call(g=[Tensor4(src[0].ptr, 256 * 8 * 128, 128, 8 * 128, 256)] + g32[1:]) == INVALID   # output over input
     assert call(gk=t4(BASE + (4 << 24), rows=100)) == INVALID
     assert call(lam=float("inf")) == INVALID
+    assert call(n=1 << 23) == UNSUPPORTED      # 2^31 four-element vectors: beyond the 32-bit index
     # one fp32 partial per weight per workgroup of 256 threads x 4 four-element vectors
     assert Y.yoco_compose_backward_workspace_size(1, 256, 8, 128, BF16) == ((256 * 8 * 32 + 1023) // 1024) * 16
     assert Y.yoco_compose_backward_workspace_size(1, 3, 1, 64, F32) == 16
