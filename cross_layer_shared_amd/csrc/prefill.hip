@@ -6,11 +6,18 @@
 // Dense contraction on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 // A workgroup of 8 wavefronts serves 8 (head, 32-query block) slots that share
 // one kv head (4 heads x 2 consecutive query blocks); it streams the cache in
-// 128-key tiles staged through LDS (two stages, one barrier per tile), so that
-// all eight wavefronts read each tile from LDS instead of from memory. K and V
-// are both stored row-major; the V operand of the PV product is read with the
-// gfx950 transposing LDS read (ds_read_b64_tr_b16), which hands each lane 4
+// 128-key tiles staged through LDS (two K and two V slots), so that all eight
+// wavefronts read each tile from LDS instead of from memory. K and V are both
+// stored row-major; the V operand of the PV product is read with the gfx950
+// transposing LDS read (ds_read_b64_tr_b16), which hands each lane 4
 // consecutive keys of one dim.
+//
+// The two wavefronts on each SIMD (waves w and w + 4) run half a tile apart:
+// while one issues the MFMAs of a tile (PV of the previous tile, scores of
+// this one) the other runs the softmax of its tile on the VALU and the
+// exponential unit, and the workgroup barrier between the halves swaps the
+// roles. Run in step instead, both wavefronts would wait on the matrix core
+// at the same time and then both on the VALU.
 //
 // Per wavefront and tile:
 //   S^T = K Q^T   (4 x 32 keys by 32 queries; D = 128 in 8 MFMA k-steps)
@@ -22,8 +29,8 @@
 // rows of each 32-key block are fed to the MFMA in the order that swaps bits 2
 // and 3 of the key index, which makes the 8 P values a lane holds for one PV
 // k-step 8 consecutive keys: two transposing reads of 4 keys each.
-// Probabilities are rounded to bf16 for the PV product; the normaliser sums
-// the same fp32 values.
+// Probabilities are rounded to bf16 for the PV product, and the normaliser
+// sums the same rounded values.
 //
 // Every workgroup of one (sequence, kv head) streams the same K and V tiles,
 // so the tiles are loaded through the L2 (temporal loads), and the 1-D grid is
@@ -42,8 +49,9 @@ namespace {
 constexpr int kWaves = 8;             // 4 heads x 2 query blocks; one workgroup per CU
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 32;               // queries per wavefront
-constexpr int kKT = 128;              // keys per tile (two LDS stages: 148 KiB at D = 128)
+constexpr int kKT = 128;              // keys per tile (two slots each of K and V: 148 KiB at D = 128)
 constexpr int kNB = kKT / 32;         // 32-key MFMA blocks per tile
+constexpr float kLazy = 8.f;          // rescale threshold of the running max (log2 units)
 
 // Sizes that follow the head dimension (D = 64 or 128).
 template <int D>
@@ -145,34 +153,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int64_t kst = p.k.st * 2, vst = p.v.st * 2;
   const char* kbase = static_cast<const char*>(p.k.ptr) + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh + ld_d) * 2;
   const char* vbase = static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh + ld_d) * 2;
-  u32x4 kreg[kKPT], vreg[kKPT];
-  auto load_tile = [&](int t) {
+  auto load_rows = [&](u32x4* reg, const char* base, int64_t st, int t) {
     const int row0 = t * kKT + ld_k;
     if (t * kKT + kKT <= kv_len) {          // whole tile inside the cache prefix: no clamping
-      const char* kp = kbase + row0 * kst;
-      const char* vp = vbase + row0 * vst;
+      const char* ptr = base + row0 * st;
 #pragma unroll
-      for (int i = 0; i < kKPT; ++i) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kp + i * kst);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vp + i * vst);
-      }
+      for (int i = 0; i < kKPT; ++i) reg[i] = *reinterpret_cast<const u32x4*>(ptr + i * st);
     } else {
 #pragma unroll
-      for (int i = 0; i < kKPT; ++i) {
-        const int row = min(row0 + i, kv_len - 1);
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + row * kst);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + row * vst);
-      }
+      for (int i = 0; i < kKPT; ++i) reg[i] = *reinterpret_cast<const u32x4*>(base + min(row0 + i, kv_len - 1) * st);
     }
   };
-  auto store_tile = [&](int stage) {
-    __bf16* kl = lds + stage * kStage;
-    __bf16* vl = kl + kKT * kKPad;
+  // K tile t lives in K slot t % 2 and V tile t in V slot t % 2.
+  auto k_slot = [&](int t) { return lds + (t & 1) * kStage; };
+  auto v_slot = [&](int t) { return lds + (t & 1) * kStage + kKT * kKPad; };
+  auto store_k = [&](const u32x4* reg, int t) {
+    __bf16* kl = k_slot(t);
 #pragma unroll
-    for (int i = 0; i < kKPT; ++i) {
-      *reinterpret_cast<u32x4*>(&kl[(ld_k + i) * kKPad + ld_d]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&vl[(ld_k + i) * kVPad + ld_d]) = vreg[i];
-    }
+    for (int i = 0; i < kKPT; ++i) *reinterpret_cast<u32x4*>(&kl[(ld_k + i) * kKPad + ld_d]) = reg[i];
+  };
+  auto store_v = [&](const u32x4* reg, int t) {
+    __bf16* vl = v_slot(t);
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i) *reinterpret_cast<u32x4*>(&vl[(ld_k + i) * kVPad + ld_d]) = reg[i];
   };
 
   // Lane roles of the transposing V reads: group gq = lane/16, s = lane%16 addresses
@@ -190,16 +193,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float m_run = -INFINITY;   // running max of scaled scores (log2 domain)
   float l_run = 0.f;         // this lane's share of the running sum
   const float sl = p.scale_log2;
+  f32x16 sc[kNB];            // raw scores of the current tile (S^T blocks)
+  bf16x8 pb[kNB][2];         // bf16 probabilities of the current tile (P^T operands)
 
-  // One tile of kKT keys: scores, online softmax, PV, and the hand-over of the next tile.
-  auto tile = [&]<bool MASKED>(int t) {
-    const int stage = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    const __bf16* kl = lds + stage * kStage;
-    const __bf16* vl = kl + kKT * kKPad;
-
-    // ---- S^T = K Q^T for kNB blocks of 32 keys (raw dot products) ----
-    f32x16 sc[kNB];
+  // ---- S^T = K Q^T for kNB blocks of 32 keys (raw dot products) ----
+  auto scores = [&](int t) {
+    const __bf16* kl = k_slot(t);
 #pragma unroll
     for (int hb = 0; hb < kNB; ++hb)
 #pragma unroll
@@ -212,66 +211,123 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[hb], 0, 0, 0);
       }
     }
-    // Schedule: the K fragment reads run four ahead of the MFMAs that use them
-    // (the default schedule keeps one or two ahead; +1-2% measured).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // 4 LDS reads
+  };
+  // Schedules of the MFMA phase (0x008: MFMA, 0x100: LDS read). A wavefront
+  // runs this phase while the other wavefront of its SIMD is in its softmax
+  // phase, so the operand reads must run well ahead of the MFMAs that use
+  // them: PV operands (two reads per MFMA) kAP MFMAs ahead, K fragments (one
+  // read per MFMA) 2 kAP ahead.
+  constexpr int kAP = 4;
+  constexpr int kNS = kNQ * kNB;        // MFMAs of the scores
+  constexpr int kNP = kNB * 2 * kNDB;   // MFMAs of the PV product
+  auto sched_scores = [] {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAP, 0);
 #pragma unroll
-    for (int i = 0; i < kNQ * kNB - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // 1 LDS read
+    for (int i = 0; i < kNS - 2 * kAP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);   // the last 4 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAP, 0);
+  };
+  auto sched_pv_scores = [] {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAP, 0);
+#pragma unroll
+    for (int i = 0; i < kNP; ++i) {   // the last kAP of these fetch the first 2 kAP K fragments
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kNS - 2 * kAP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAP, 0);
+  };
+  auto sched_pv = [] {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAP, 0);
+#pragma unroll
+    for (int i = 0; i < kNP - kAP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAP, 0);
+  };
 
-    // ---- causal mask (diagonal tiles only), tile max ----
-    if constexpr (MASKED) {
-      const int key0 = t * kKT;
-#pragma unroll
-      for (int hb = 0; hb < kNB; ++hb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * hb + perm_key(8 * (r >> 2) + 4 * q + (r & 3));
-          if (key > pos) sc[hb][r] = -INFINITY;
-        }
-    }
-    float mt = -INFINITY;
+  // ---- causal mask (diagonal tiles only), online softmax, bf16 P^T operands ----
+  auto mask = [&](int t) {
+    // key offsets within the tile are constants per register (plus 8 on the
+    // upper lane half: its bit 2 lands on bit 3), compared against one
+    // per-tile limit
+    const int lim = pos - t * kKT - 8 * q;
 #pragma unroll
     for (int hb = 0; hb < kNB; ++hb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[hb][r]);
+      for (int r = 0; r < 16; ++r)
+        if (32 * hb + perm_key(8 * (r >> 2) + (r & 3)) > lim) sc[hb][r] = -INFINITY;
+  };
+  // Tile max and the lazy rescale; returns the reference max the
+  // exponentials subtract.
+  auto softmax_max = [&]() {
+    // tile max: four chains of three-input maxima, one per 32-key block
+    float mb[kNB];
+#pragma unroll
+    for (int hb = 0; hb < kNB; ++hb) {
+      float m = fmaxf(sc[hb][0], sc[hb][1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) m = fmaxf(fmaxf(m, sc[hb][r]), sc[hb][r + 1]);
+      mb[hb] = m;
+    }
     // the scale is positive, so the max of the scaled scores is the scaled max
-    mt = xor32_max(mt) * sl;
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-      const float alpha = fast_exp2(m_run - m_use);
+    const float mt = xor32_max(fmaxf(fmaxf(mb[0], mb[1]), fmaxf(mb[2], mb[3]))) * sl;
+    // Lazy rescaling: the reference max m_run only moves when some row's
+    // tile max exceeds it by more than kLazy (log2 units), so exponentials
+    // stay below 2^kLazy and the accumulators are rescaled in few tiles.
+    // Numerator and normaliser share the reference, so the result is exact
+    // up to rounding for any choice of it.
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < kNDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[db][r] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
-
-    // ---- P = exp2(scale * S - m), row sums, bf16 P^T operands ----
-    bf16x8 pb[kNB][2];
+    return (m_run == -INFINITY) ? 0.f : m_run;
+  };
+  // P = exp2(scale * S - m) rounded to bf16 pairs; the normaliser sums the
+  // rounded values (the ones the PV product uses) with dot2 against (1, 1).
+  // hook(i) runs before the i-th of the 2 kNB chunks of eight exponentials.
+  auto softmax_exp = [&](float m_use, auto&& hook) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls[kNB][2];
 #pragma unroll
     for (int hb = 0; hb < kNB; ++hb) {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
+        hook(2 * hb + hs);
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p0v = fast_exp2(__builtin_fmaf(sc[hb][8 * hs + 2 * e], sl, -m_use));
           const float p1v = fast_exp2(__builtin_fmaf(sc[hb][8 * hs + 2 * e + 1], sl, -m_use));
-          l_run += p0v + p1v;
           w[e] = pack2(p0v, p1v);
         }
+        float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0]), ones, 0.f, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[1]), ones, a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2]), ones, a, false);
+        ls[hb][hs] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[3]), ones, a, false);
         u32x4 wv = {w[0], w[1], w[2], w[3]};
         pb[hb][hs] = __builtin_bit_cast(bf16x8, wv);
       }
     }
+    l_run += ((ls[0][0] + ls[0][1]) + (ls[1][0] + ls[1][1])) + ((ls[2][0] + ls[2][1]) + (ls[3][0] + ls[3][1]));
+  };
 
-    // ---- O^T += V^T P^T ----
+  // ---- O^T += V^T P^T ----
+  auto pv = [&](int t) {
+    const __bf16* vl = v_slot(t);
 #pragma unroll
     for (int hb = 0; hb < kNB; ++hb) {
 #pragma unroll
@@ -288,21 +344,93 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
     }
-
-    if (t + 1 < n_tiles) store_tile(stage ^ 1);
-    __syncthreads();
   };
 
-  // Tiles before first_masked hold only keys <= every query position of the workgroup.
-  const int first_masked = min((p.p0 + c_wg) / kKT, n_tiles);
-  load_tile(0);
-  store_tile(0);
-  // Every load issued so far (Q and the first tile) is complete here, so the
-  // loop's waits only cover the tile prefetched inside it.
+  // Two wavefront groups (waves 0-3 and 4-7: one of each on every SIMD) run
+  // half a tile apart. Per tile a wavefront has an MFMA phase (PV of the
+  // previous tile, then the scores of this one) and a softmax phase (VALU and
+  // the exponential unit); the workgroup advances in intervals separated by a
+  // barrier, and in each interval one group is in its MFMA phase while the
+  // other is in its softmax phase, so the two kinds of work overlap on every
+  // SIMD. Group 1 starts one interval late. The group in its softmax phase
+  // also moves its half of the key rows of K tile s+1 and V tile s
+  // (s = interval / 2) from memory into their LDS slots: K slot (s+1) % 2 was
+  // last read by the scores of tile s-1 and V slot s % 2 by the PV of tile
+  // s-2, both finished by the end of interval 2s-1, and the first reads of
+  // the new tiles come in interval 2s+2.
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int first_masked = min((p.p0 + c_wg) / kKT, n_tiles);   // earlier tiles need no causal mask
+  {
+    u32x4 kr[kKPT], vr[kKPT];
+    load_rows(kr, kbase, kst, 0);
+    load_rows(vr, vbase, vst, 0);
+    store_k(kr, 0);
+    store_v(vr, 0);
+    if (n_tiles > 1) {
+      load_rows(kr, kbase, kst, 1);
+      store_k(kr, 1);
+    }
+  }
+  // Every load issued so far (Q and the first tiles) is complete here.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  for (int t = 0; t < first_masked; ++t) tile.template operator()<false>(t);
-  for (int t = first_masked; t < n_tiles; ++t) tile.template operator()<true>(t);
+  // The softmax phase of tile t, with the copy duty of interval 2t + 1 + grp.
+  // One of the 2 kKPT row loads goes out before each chunk of eight
+  // exponentials (spread out like this the phase ran faster than with all
+  // loads issued at its start). Rows past the cache prefix are clamped, so
+  // every request is valid; outside the duty the rows are not stored.
+  auto softmax_phase = [&](int t) {
+    const int s = t + grp;
+    const bool mk = s >= 1 && s + 1 < n_tiles;
+    const bool mv = s >= 1 && s < n_tiles;
+    if (t >= first_masked) mask(t);
+    const float m_use = softmax_max();
+    u32x4 kr[kKPT], vr[kKPT];   // this thread's rows of the tiles in flight
+    const int krow0 = (s + 1) * kKT + ld_k, vrow0 = s * kKT + ld_k;
+    softmax_exp(m_use, [&](int i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < kKPT)
+        kr[i] = *reinterpret_cast<const u32x4*>(kbase + min(krow0 + i, kv_len - 1) * kst);
+      else if (i < 2 * kKPT)
+        vr[i - kKPT] = *reinterpret_cast<const u32x4*>(vbase + min(vrow0 + i - kKPT, kv_len - 1) * vst);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // The probabilities are only read in the next phase; without this the
+    // compiler sinks their computation below the LDS stores, whose wait for
+    // the tile loads would then stall the wavefront with nothing to overlap.
+#pragma unroll
+    for (int hb = 0; hb < kNB; ++hb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) asm volatile("" : "+v"(pb[hb][hs]));
+    if (mk) store_k(kr, s + 1);
+    if (mv) store_v(vr, s);
+  };
+  // Group 0: MFMA(t) in interval 2t, softmax(t) in 2t+1, last PV in 2n.
+  // Group 1: one interval later. Both pass 2n+1 barriers. The scheduling
+  // fences keep every MFMA and exponential inside its own interval: the
+  // compiler would otherwise sink the last MFMAs of a phase past the barrier.
+  auto interval_end = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (grp) interval_end();
+  scores(0);
+  sched_scores();
+  interval_end();
+  softmax_phase(0);
+  interval_end();
+  for (int t = 1; t < n_tiles; ++t) {
+    pv(t - 1);
+    scores(t);
+    sched_pv_scores();
+    interval_end();
+    softmax_phase(t);
+    interval_end();
+  }
+  pv(n_tiles - 1);
+  sched_pv();
+  if (!grp) interval_end();
 
   // ---- normalise and write ----
   const float l_tot = xor32_sum(l_run);
