@@ -12,12 +12,13 @@
 // transposing LDS read (ds_read_b64_tr_b16), which hands each lane 4
 // consecutive keys of one dim.
 //
-// The two wavefronts on each SIMD (waves w and w + 4) run half a tile apart:
-// while one issues the MFMAs of a tile (PV of the previous tile, scores of
-// this one) the other runs the softmax of its tile on the VALU and the
-// exponential unit, and the workgroup barrier between the halves swaps the
-// roles. Run in step instead, both wavefronts would wait on the matrix core
-// at the same time and then both on the VALU.
+// At D = 128 the two wavefronts on each SIMD (waves w and w + 4) run half a
+// tile apart: while one issues the MFMAs of a tile (PV of the previous tile,
+// scores of this one) the other runs the softmax of its tile on the VALU and
+// the exponential unit, and the workgroup barrier between the halves swaps
+// the roles. Run in step instead, both wavefronts would wait on the matrix
+// core at the same time and then both on the VALU. At D = 64 the MFMA phase
+// is half as long and the softmax phase dominates; there they run in step.
 //
 // Per wavefront and tile:
 //   S^T = K Q^T   (4 x 32 keys by 32 queries; D = 128 in 8 MFMA k-steps)
@@ -346,19 +347,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  // Two wavefront groups (waves 0-3 and 4-7: one of each on every SIMD) run
-  // half a tile apart. Per tile a wavefront has an MFMA phase (PV of the
-  // previous tile, then the scores of this one) and a softmax phase (VALU and
-  // the exponential unit); the workgroup advances in intervals separated by a
-  // barrier, and in each interval one group is in its MFMA phase while the
-  // other is in its softmax phase, so the two kinds of work overlap on every
-  // SIMD. Group 1 starts one interval late. The group in its softmax phase
-  // also moves its half of the key rows of K tile s+1 and V tile s
-  // (s = interval / 2) from memory into their LDS slots: K slot (s+1) % 2 was
-  // last read by the scores of tile s-1 and V slot s % 2 by the PV of tile
-  // s-2, both finished by the end of interval 2s-1, and the first reads of
-  // the new tiles come in interval 2s+2.
+  // Two wavefront groups (waves 0-3 and 4-7: one of each on every SIMD). Per
+  // tile a wavefront has an MFMA phase (PV of the previous tile, then the
+  // scores of this one) and a softmax phase (VALU and the exponential unit).
+  // At D = 128 the workgroup advances in intervals separated by a barrier, and
+  // in each interval one group is in its MFMA phase while the other is in its
+  // softmax phase, so the two kinds of work overlap on every SIMD; group 1
+  // starts one interval late. The group in its softmax phase also moves its
+  // half of the key rows of K tile s+1 and V tile s (s = interval / 2) from
+  // memory into their LDS slots: K slot (s+1) % 2 was last read by the scores
+  // of tile s-1 and V slot s % 2 by the PV of tile s-2, both finished by the
+  // end of interval 2s-1, and the first reads of the new tiles come in
+  // interval 2s+2.
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  constexpr bool kStagger = (D == 128);   // the two groups half a tile apart
   const int first_masked = min((p.p0 + c_wg) / kKT, n_tiles);   // earlier tiles need no causal mask
   {
     u32x4 kr[kKPT], vr[kKPT];
@@ -374,13 +376,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // Every load issued so far (Q and the first tiles) is complete here.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  // The softmax phase of tile t, with the copy duty of interval 2t + 1 + grp.
+  // The softmax phase of tile t, with the copy duty s = t (+ grp when staggered).
   // One of the 2 kKPT row loads goes out before each chunk of eight
   // exponentials (spread out like this the phase ran faster than with all
   // loads issued at its start). Rows past the cache prefix are clamped, so
   // every request is valid; outside the duty the rows are not stored.
   auto softmax_phase = [&](int t) {
-    const int s = t + grp;
+    const int s = t + (kStagger ? grp : 0);
     const bool mk = s >= 1 && s + 1 < n_tiles;
     const bool mv = s >= 1 && s < n_tiles;
     if (t >= first_masked) mask(t);
@@ -405,32 +407,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (mk) store_k(kr, s + 1);
     if (mv) store_v(vr, s);
   };
-  // Group 0: MFMA(t) in interval 2t, softmax(t) in 2t+1, last PV in 2n.
-  // Group 1: one interval later. Both pass 2n+1 barriers. The scheduling
-  // fences keep every MFMA and exponential inside its own interval: the
-  // compiler would otherwise sink the last MFMAs of a phase past the barrier.
+  // Staggered (D = 128): group 0 runs MFMA(t) in interval 2t, softmax(t) in
+  // 2t+1 and the last PV in 2n; group 1 runs one interval later; both pass
+  // 2n+1 barriers. In step (D = 64, where the softmax phase outweighs the
+  // MFMA phase so much that two softmax phases side by side hide each
+  // other's latency better): both groups run the same phase, and one barrier
+  // per tile, after the softmax phase, is enough, since the copy duty of
+  // interval 2t+1 writes slots last read in interval 2t-2. The scheduling
+  // fences keep every MFMA and exponential inside its own phase: the compiler
+  // would otherwise sink the last MFMAs of a phase past the barrier.
   auto interval_end = [] {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  if (grp) interval_end();
+  auto phase_end = [&] {
+    if constexpr (kStagger)
+      interval_end();
+    else
+      __builtin_amdgcn_sched_barrier(0);
+  };
+  if (kStagger && grp) interval_end();
   scores(0);
   sched_scores();
-  interval_end();
+  phase_end();
   softmax_phase(0);
   interval_end();
   for (int t = 1; t < n_tiles; ++t) {
     pv(t - 1);
     scores(t);
     sched_pv_scores();
-    interval_end();
+    phase_end();
     softmax_phase(t);
     interval_end();
   }
   pv(n_tiles - 1);
   sched_pv();
-  if (!grp) interval_end();
+  if (kStagger && !grp) interval_end();
 
   // ---- normalise and write ----
   const float l_tot = xor32_sum(l_run);
