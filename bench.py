@@ -73,7 +73,7 @@ class Flusher:
 
 
 def timed(torch, fn, reps, flush=None):
-    """Average duration (ms) of fn() over reps launches, HIP events on the current stream."""
+    """Median and minimum duration (ms) of fn() over reps launches, HIP events on the current stream."""
     durs = []
     for _ in range(reps):
         if flush is not None:
@@ -84,7 +84,7 @@ def timed(torch, fn, reps, flush=None):
         b.record()
         b.synchronize()
         durs.append(a.elapsed_time(b))
-    return float(np.mean(durs)), float(np.min(durs))
+    return float(np.median(durs)), float(np.min(durs))
 
 
 # ----------------------------------------------------------------- headline
