@@ -143,3 +143,24 @@ def test_full_chunked_prefill_workload():
     say(f"  {len(rows)} sampled rows")
     o_ref, lse_ref = O.causal_prefill(q, k, v, 0, rows=rows)
     _compare(o, lse, o_ref, lse_ref, rows=rows)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes(case):
+    """Seeded random shapes: batch 1-3, 1-4 kv heads, group sizes 1-8, D = 64 or
+    128, chunks of 1-300 rows at offsets 0-400 in caches with spare rows, so
+    tile counts, ragged query blocks and both wavefront schedules (staggered
+    at D = 128, in step at D = 64) vary together."""
+    r = np.random.default_rng(1000 + case)
+    B = int(r.integers(1, 4))
+    Hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4, 8]))
+    D = int(r.choice([64, 128]))
+    C = int(r.integers(1, 301))
+    p0 = int(r.integers(0, 401))
+    spare = int(r.integers(0, 21))
+    say(f"  B={B} Hkv={Hkv} G={G} D={D} C={C} p0={p0} spare={spare}")
+    q, k, v = _inputs(B, C, Hkv * G, Hkv, p0 + C + spare, 2000 + case, D=D)
+    o, lse = _prefill(dev(q), dev(k), dev(v), p0)
+    o_ref, lse_ref = O.causal_prefill(q, k, v, p0)
+    _compare(o, lse, o_ref, lse_ref)
