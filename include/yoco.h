@@ -285,8 +285,9 @@ yoco_status yoco_decode_merge(const void* workspace, size_t workspace_bytes, int
  * does, so the query at absolute position p attends to cache rows [0, p]
  * (inclusive: its own composed KV is already in the cache); [YOCO++] section
  * 3: prefill is compute-bound. A chunk holds C query rows at positions [p0, p0 + C).
- * QK^T and PV run on bf16 MFMA with fp32 accumulation; the softmax is fp32
- * and the probabilities are rounded to bf16 for the PV product.
+ * QK^T and PV run on bf16 MFMA with fp32 accumulation; the softmax is fp32,
+ * the probabilities are rounded to bf16 for the PV product and the normaliser
+ * sums those rounded values.
  *
  *   q          [B, C, Hq, D] contiguous bf16.
  *   k_cache, v_cache  bf16; rows [0, p0 + C) are read; p0 + C <= rows.
