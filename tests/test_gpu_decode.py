@@ -117,6 +117,27 @@ def test_group_sizes_and_head_dims(G, D, dtype):
     _compare(o, lse, o_ref, lse_ref, dtype)
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes(case):
+    """Seeded random shapes: batch 1-4, 1-4 kv heads, group sizes 1-16, D = 64
+    or 128, bf16 or fp32 caches, 1-3000 rows, automatic or explicit split
+    counts, and per-sequence lengths on every other case."""
+    r = np.random.default_rng(3000 + case)
+    B = int(r.integers(1, 5))
+    Hkv = int(r.integers(1, 5))
+    G = int(r.choice([1, 2, 4, 8, 16]))
+    D = int(r.choice([64, 128]))
+    dtype = str(r.choice(["bf16", "f32"]))
+    T = int(r.integers(1, 3001))
+    splits = 0 if case % 3 == 0 else int(r.integers(1, min(T, 16) + 1))
+    lens = [int(x) for x in r.integers(1, T + 1, size=B)] if case % 2 else None
+    say(f"  B={B} Hkv={Hkv} G={G} D={D} {dtype} T={T} splits={splits} lens={lens}")
+    q, k, v = _inputs(B, T, G * Hkv, Hkv, D, dtype, 4000 + case)
+    o, lse = _decode(dev(q), dev(k), dev(v), splits, seq_lens=lens)
+    o_ref, lse_ref = O.decode_attention(q, k, v, seq_lens=None if lens is None else np.array(lens))
+    _compare(o, lse, o_ref, lse_ref, dtype)
+
+
 @pytest.mark.parametrize("splits", [1, 5, 0])
 def test_ragged_seq_lens(splits):
     """Per-sequence lengths (clamped to [1, T] on the device); rows past a length never matter."""
