@@ -1,4 +1,5 @@
-"""Build libyoco.so (the gfx950 HIP kernels and their C ABI) in the package folder.
+"""Build libyoco.so (the gfx950 HIP kernels and their C ABI) and
+libyoco_ceiling.so (the achievable-bandwidth probes) in the package folder.
 
 Run as ``python -m cross_layer_shared_amd.build`` or call ``build()``. Every
 call recompiles; objects go to ``_build/`` at the repository root.
@@ -18,6 +19,8 @@ OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libyoco.so")
 SOURCES = ["yoco_api.cpp", "compose.hip", "compose_backward.hip", "decode.hip", "decode_cor.hip", "decode_append.hip",
            "prefill.hip"]
+CEILING_LIB = os.path.join(PKG, "libyoco_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are switched off for the device code (the target
@@ -47,18 +50,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs: list[str]) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES) + len(CEILING_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + CEILING_SOURCES))
+    _link(LIB, objs[:len(SOURCES)])
+    _link(CEILING_LIB, objs[len(SOURCES):])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

@@ -1,0 +1,67 @@
+"""Python binding of libyoco_ceiling.so (achievable-bandwidth probes): argument
+marshalling only, like the binding of libyoco.so. The probes are plain
+streaming kernels with the traffic pattern of the decode (one read of a buffer)
+and of the compose (four reads, two writes) and none of the method's
+arithmetic; the benchmark times them beside the kernels they bound."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .binding import YocoError, _stream
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+CEILING_LIB_PATH = os.path.join(_HERE, "libyoco_ceiling.so")
+CEILING_EXPORTED = ("yoco_ceiling_read", "yoco_ceiling_read4_write2", "yoco_ceiling_last_error")
+
+_lib = None
+
+
+def load_ceiling_library(path: str = CEILING_LIB_PATH) -> ctypes.CDLL:
+    """Load libyoco_ceiling.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m cross_layer_shared_amd.build`")
+    lib = ctypes.CDLL(path)
+    i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.yoco_ceiling_read.argtypes = [vp, sz, i, i, i, vp, vp]
+    lib.yoco_ceiling_read.restype = i
+    lib.yoco_ceiling_read4_write2.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, vp]
+    lib.yoco_ceiling_read4_write2.restype = i
+    lib.yoco_ceiling_last_error.argtypes = []
+    lib.yoco_ceiling_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise YocoError(status, load_ceiling_library().yoco_ceiling_last_error().decode())
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    if not t.is_contiguous():
+        raise ValueError("probe buffers must be contiguous")
+    return t.numel() * t.element_size()
+
+
+def yoco_ceiling_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int = 256, threads: int = 512,
+                      nontemporal: bool = True, stream=None) -> None:
+    """Read every byte of src once (see yoco_ceiling.h); sink is a device int32/uint32 [>= 1]."""
+    _check(load_ceiling_library().yoco_ceiling_read(src.data_ptr(), _nbytes(src), int(workgroups), int(threads),
+                                                    int(bool(nontemporal)), sink.data_ptr(), _stream(stream)))
+
+
+def yoco_ceiling_read4_write2(a, b, c, d, e, f, threads: int = 512, stream=None) -> None:
+    """e = a + b, f = c + d as 32-bit integers; six equally sized contiguous buffers."""
+    n = _nbytes(a)
+    for t in (b, c, d, e, f):
+        if _nbytes(t) != n:
+            raise ValueError("the six buffers must have the same size")
+    _check(load_ceiling_library().yoco_ceiling_read4_write2(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
+                                                            e.data_ptr(), f.data_ptr(), n, int(threads),
+                                                            _stream(stream)))

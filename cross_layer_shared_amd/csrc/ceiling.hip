@@ -1,0 +1,154 @@
+// Achievable-bandwidth probes (libyoco_ceiling.so): plain streaming kernels
+// with the traffic pattern of the decode (one read of a buffer, 16-byte loads,
+// several in flight per thread) and of the compose (four input streams, two
+// output streams, one 16-byte vector of each per thread), and none of the
+// method's arithmetic. The YOCO++ technical summary, section 3, prices decode
+// and composition in bytes moved; these kernels give the time those bytes take
+// on this chip when nothing else is done with them.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/yoco_ceiling.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kUnroll = 4;            // loads in flight per thread per iteration
+constexpr int kStrideWorkgroups = 2048;
+constexpr uint32_t kSinkKey = 0x9E3779B9u;
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+__device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// Workgroup w reads vectors [w * per_wg, min((w + 1) * per_wg, n)), or, with
+// per_wg = 0, every thread strides over all n vectors.
+template <bool NT>
+__global__ __launch_bounds__(1024) void read_kernel(const u32x4* __restrict__ src, uint64_t n, uint64_t per_wg,
+                                                    uint32_t* __restrict__ sink) {
+  const uint64_t nt = blockDim.x;
+  uint64_t lo, hi, step;
+  if (per_wg) {
+    lo = (uint64_t)blockIdx.x * per_wg + threadIdx.x;
+    hi = min((uint64_t)(blockIdx.x + 1) * per_wg, n);
+    step = nt;
+  } else {
+    lo = (uint64_t)blockIdx.x * nt + threadIdx.x;
+    hi = n;
+    step = (uint64_t)gridDim.x * nt;
+  }
+  uint32_t acc = 0;
+  for (uint64_t i = lo; i < hi; i += kUnroll * step) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t k = i + u * step;
+      v[u] = k < hi ? load16<NT>(src + k) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= fold(v[u]);
+  }
+  if (acc == kSinkKey) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(1024) void read4_write2_kernel(const u32x4* __restrict__ a, const u32x4* __restrict__ b,
+                                                            const u32x4* __restrict__ c, const u32x4* __restrict__ d,
+                                                            u32x4* __restrict__ e, u32x4* __restrict__ f, uint64_t n) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const u32x4 va = __builtin_nontemporal_load(a + i), vb = __builtin_nontemporal_load(b + i);
+  const u32x4 vc = __builtin_nontemporal_load(c + i), vd = __builtin_nontemporal_load(d + i);
+  __builtin_nontemporal_store(va + vb, e + i);
+  __builtin_nontemporal_store(vc + vd, f + i);
+}
+
+thread_local char g_err[256] = "";
+
+yoco_status fail(yoco_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+yoco_status launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(YOCO_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return YOCO_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_threads(int t) { return t >= 64 && t <= 1024 && t % 64 == 0; }
+
+bool overlap(const void* x, const void* y, size_t n) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+  return a < b + n && b < a + n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* yoco_ceiling_last_error(void) { return g_err; }
+
+yoco_status yoco_ceiling_read(const void* src, size_t bytes, int workgroups, int threads, int nontemporal,
+                              uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return fail(YOCO_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(src)) return fail(YOCO_ERR_ALIGNMENT, "src not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "sink not 4-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(YOCO_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (workgroups < 0 || workgroups > (1 << 20)) return fail(YOCO_ERR_INVALID_ARG, "workgroups out of range");
+  if (!valid_threads(threads)) return fail(YOCO_ERR_INVALID_ARG, "threads must be 64..1024, a multiple of 64");
+  const uint64_t n = bytes / 16;
+  const uint64_t per_wg = workgroups ? (n + workgroups - 1) / workgroups : 0;
+  const dim3 grid(workgroups ? workgroups : kStrideWorkgroups);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  if (nontemporal)
+    read_kernel<true><<<grid, threads, 0, stream>>>(s, n, per_wg, sink);
+  else
+    read_kernel<false><<<grid, threads, 0, stream>>>(s, n, per_wg, sink);
+  return launched("ceiling read");
+}
+
+yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* c, const void* d, void* e, void* f,
+                                      size_t bytes, int threads, hipStream_t stream) {
+  const void* ins[4] = {a, b, c, d};
+  void* outs[2] = {e, f};
+  for (const void* p : ins)
+    if (!p) return fail(YOCO_ERR_INVALID_ARG, "null pointer");
+  for (void* p : outs)
+    if (!p) return fail(YOCO_ERR_INVALID_ARG, "null pointer");
+  for (const void* p : ins)
+    if (!aligned16(p)) return fail(YOCO_ERR_ALIGNMENT, "a source is not 16-byte aligned");
+  for (void* p : outs)
+    if (!aligned16(p)) return fail(YOCO_ERR_ALIGNMENT, "a destination is not 16-byte aligned");
+  if (bytes == 0 || bytes % 16 || bytes >= (1ull << 35))
+    return fail(YOCO_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 below 2^35");
+  if (!valid_threads(threads)) return fail(YOCO_ERR_INVALID_ARG, "threads must be 64..1024, a multiple of 64");
+  for (void* o : outs)
+    for (const void* p : ins)
+      if (overlap(o, p, bytes)) return fail(YOCO_ERR_INVALID_ARG, "a destination overlaps a source");
+  if (overlap(e, f, bytes)) return fail(YOCO_ERR_INVALID_ARG, "the destinations overlap");
+  const uint64_t n = bytes / 16;
+  const dim3 grid((unsigned)((n + threads - 1) / threads));
+  read4_write2_kernel<<<grid, threads, 0, stream>>>(
+      static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), static_cast<const u32x4*>(c),
+      static_cast<const u32x4*>(d), static_cast<u32x4*>(e), static_cast<u32x4*>(f), n);
+  return launched("ceiling read4_write2");
+}
+
+}  // extern "C"

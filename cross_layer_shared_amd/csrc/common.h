@@ -43,7 +43,7 @@ struct DecodeParams {
   float scale_log2;       // softmax scale * log2(e)
   int num_splits;
   int rows_per_split;
-  int waves;              // wavefronts per workgroup: 4, 8 or 16
+  int waves;              // wavefronts per workgroup: 4 or 8
   bool prefetch;          // double-buffered row loads (short splits)
   float* out;             // [B, Hq, D] (used when num_splits == 1)
   float* lse;             // [B, Hq] or null (used when num_splits == 1)

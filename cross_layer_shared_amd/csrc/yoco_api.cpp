@@ -220,10 +220,6 @@ static DecodeShape decode_shape(int B, int T, int Hkv, int S_req) {
   sh.splits = (int)((T + (int64_t)rps - 1) / rps);   // drop splits the rounding leaves empty
   sh.prefetch = rps <= 2 * kDecodeShortSplit;
   sh.waves = !sh.prefetch || rps >= 8 * kDecodeMinRowsPerWave ? 8 : 4;
-#ifdef YOCO_FORCE_DECODE_WAVES
-  sh.waves = YOCO_FORCE_DECODE_WAVES;
-  sh.prefetch = true;
-#endif
   return sh;
 }
 

@@ -1,0 +1,66 @@
+/*
+ * yoco_ceiling.h - achievable-bandwidth probes of MI355X (gfx950), the
+ * yardsticks the HBM-bound kernels of libyoco.so are measured against.
+ *
+ * The YOCO++ technical summary, section 3 (efficiency analysis), states the
+ * method's cost in memory traffic: decoding reads exactly one KV set per layer,
+ * and the composition adds only I/O. How close a kernel comes to those bytes'
+ * time is read against two peaks: the published 8 TB/s of HBM3E, and what a
+ * plain kernel with the same traffic pattern and no arithmetic achieves on
+ * the same chip. These probes are that plain kernel. They carry none of the
+ * method's arithmetic and are built into a library of their own,
+ * libyoco_ceiling.so.
+ *
+ * Conventions are those of yoco.h: device pointers on the current HIP device,
+ * caller-owned buffers, asynchronous launches on `stream`, no allocation, every
+ * argument checked before anything is enqueued (a yoco_status is returned and
+ * the message is readable with yoco_ceiling_last_error() on the same thread).
+ */
+#ifndef YOCO_CEILING_H
+#define YOCO_CEILING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "yoco.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * yoco_ceiling_read - stream `bytes` bytes from `src` once, as the decode
+ * streams its cache: 16-byte loads, several in flight per thread.
+ *   src          16-byte aligned; bytes a positive multiple of 16.
+ *   workgroups   > 0: workgroup w reads the w-th of `workgroups` contiguous,
+ *                equal ranges (the decode's split layout); 0: every thread
+ *                strides over the whole buffer (grid of 2048 workgroups).
+ *   threads      threads per workgroup: 64, 128, ..., 1024.
+ *   nontemporal  1: nontemporal loads (the decode's policy); 0: ordinary loads
+ *                (these allocate in the caches: a read of a buffer larger than
+ *                the 256 MB Infinity Cache evicts what it held).
+ *   sink         device uint32 [1]: written only if the XOR of all loaded
+ *                words equals a fixed 32-bit constant (keeps the loads live).
+ */
+yoco_status yoco_ceiling_read(const void* src, size_t bytes, int workgroups, int threads, int nontemporal,
+                              uint32_t* sink, hipStream_t stream);
+
+/*
+ * yoco_ceiling_read4_write2 - the compose kernel's traffic with no arithmetic:
+ * e = a + b and f = c + d as 32-bit integers over `bytes` bytes per stream,
+ * one 16-byte vector of each stream per thread, nontemporal loads and stores.
+ *   a, b, c, d   sources; e, f destinations (must not overlap the sources).
+ *   bytes        bytes per stream, a positive multiple of 16, below 2^35.
+ *   threads      threads per workgroup: 64, 128, ..., 1024.
+ */
+yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* c, const void* d, void* e, void* f,
+                                      size_t bytes, int threads, hipStream_t stream);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* yoco_ceiling_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* YOCO_CEILING_H */

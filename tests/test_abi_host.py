@@ -247,3 +247,48 @@ def _load_missing(binding, path):
         binding.load_library(path)
     finally:
         binding._lib = saved
+
+
+# ----------------------------------------------------------------- bandwidth probes
+
+CEILING_HEADER = os.path.join(ROOT, "include", "yoco_ceiling.h")
+
+
+def test_ceiling_library_exports_every_declared_symbol():
+    from cross_layer_shared_amd import ceiling as C
+    text = re.sub(r"/\*.*?\*/", "", open(CEILING_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(yoco_ceiling_[a-z_0-9]+)\s*\(", text)))
+    assert set(names) == set(C.CEILING_EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", C.CEILING_LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (yoco_\w+)", out))
+    for n in names:
+        assert n in exported, n
+    assert not any(n.startswith("yoco_") and not n.startswith("yoco_ceiling_") for n in exported)
+
+
+def test_ceiling_probes_reject_bad_arguments():
+    from cross_layer_shared_amd import ceiling as C
+    lib = C.load_ceiling_library()
+    sink = BASE + (1 << 30)
+    cases = [
+        (lib.yoco_ceiling_read(None, 1 << 20, 256, 512, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE + 8, 1 << 20, 256, 512, 1, sink, None), ALIGN),
+        (lib.yoco_ceiling_read(BASE, 1000, 256, 512, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, -1, 512, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 100, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 2048, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 512, 1, sink + 2, None), ALIGN),
+    ]
+    bufs = [BASE + (i << 24) for i in range(6)]
+    cases += [
+        (lib.yoco_ceiling_read4_write2(*bufs[:5], None, 1 << 20, 512, None), INVALID),
+        (lib.yoco_ceiling_read4_write2(*bufs[:5], bufs[5] + 4, 1 << 20, 512, None), ALIGN),
+        (lib.yoco_ceiling_read4_write2(*bufs, 0, 512, None), INVALID),
+        (lib.yoco_ceiling_read4_write2(*bufs, 1 << 20, 32, None), INVALID),
+        (lib.yoco_ceiling_read4_write2(*bufs[:4], bufs[0], bufs[5], 1 << 20, 512, None), INVALID),   # e aliases a
+        (lib.yoco_ceiling_read4_write2(*bufs[:5], bufs[4] + 16, 1 << 20, 512, None), INVALID),       # e, f overlap
+    ]
+    for got, want in cases:
+        assert got == want
+        assert lib.yoco_ceiling_last_error().decode()

@@ -8,7 +8,8 @@ import torch
 import cross_layer_shared_amd as Y
 import oracle as O
 from synthetic import inputs as S
-from tests.gpu_util import dev, host, say
+from tests import bars
+from tests.gpu_util import dev, host, host_bits, say
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +73,17 @@ def test_against_oracle_over_exact_composition(dtype, D, tol):
         assert np.max(np.max(np.abs(oa - o_ref), axis=-1) / np.max(np.abs(o_ref), axis=-1)) <= tol
     else:
         assert err <= tol and np.max(np.abs(la - lse_ref)) <= tol
+        # against the oracle over the composed values as stored (rounded to bf16 by the compose kernel,
+        # whose arithmetic the decode repeats row by row): the decode bars
+        d = {k: dev(v) for k, v in raw.items()}
+        kc, vc = torch.empty_like(d["ki"]), torch.empty_like(d["vi"])
+        Y.yoco_compose_kv(Y.head_major(d["k1"]), Y.head_major(d["ki"]), Y.head_major(d["v1"]),
+                          Y.head_major(d["vi"]), kc, vc, 0, alpha, B=w.B, n=w.T, Hkv=w.Hkv, D=w.D, dtype=1)
+        torch.cuda.synchronize()
+        o_st, lse_st = O.decode_attention(q, host_bits(kc), host_bits(vc))
+        r = bars.decode_bf16(oa, la, o_st, lse_st)
+        say("  over the stored composition: " + bars.report(r))
+        assert r["ok"], r
 
 
 def test_mid_context_shape():

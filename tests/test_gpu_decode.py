@@ -1,9 +1,10 @@
 """GPU parity of the split-K decode (yoco_cross_attn_decode, its split pass and
 merge) against the fp64 oracle.
 
-Bar: fp32 caches within 1e-5 (per (b, h) row: ||o - o_ref||_inf <= 1e-5 ||o_ref||_inf);
-bf16 caches with fp32 accumulation within 1e-2 absolute; lse within the same
-bars. The scale-normalised error ||o - o_ref||_inf / rms(o_ref) is printed."""
+Bar: fp32 caches within 1e-5 (per (b, h) row: ||o - o_ref||_inf <= 1e-5 ||o_ref||_inf,
+lse within 1e-5 relative); bf16 caches with fp32 accumulation: every output
+row within 1e-3 of its rms and lse within 1e-4 absolute, besides the stated
+1e-2 absolute (the derivation is in tests/bars.py)."""
 import numpy as np
 import pytest
 import torch
@@ -11,6 +12,7 @@ import torch
 import cross_layer_shared_amd as Y
 import oracle as O
 from synthetic import inputs as S
+from tests import bars
 from tests.gpu_util import dev, host, rowwise_rel, say
 
 pytestmark = pytest.mark.gpu
@@ -32,16 +34,14 @@ def _decode(q, k, v, splits=0, seq_lens=None, T=None):
 def _compare(o, lse, o_ref, lse_ref, dtype, mask=None):
     if mask is not None:
         o, lse, o_ref, lse_ref = o[mask], lse[mask], o_ref[mask], lse_ref[mask]
-    rms = np.sqrt(np.mean(o_ref ** 2))
-    abs_err = np.max(np.abs(o - o_ref))
-    say(f"  max|o-ref| {abs_err:.3e}  /rms {abs_err / rms:.3e}  row-rel {rowwise_rel(o, o_ref):.3e}  "
-        f"max|lse-ref| {np.max(np.abs(lse - lse_ref)):.3e}")
     if dtype == "f32":
+        say(f"  row-rel {rowwise_rel(o, o_ref):.3e}  max|lse-ref| {np.max(np.abs(lse - lse_ref)):.3e}")
         assert rowwise_rel(o, o_ref) <= F32_RTOL
         assert np.max(np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))) <= F32_RTOL
     else:
-        assert abs_err <= BF16_ATOL
-        assert np.max(np.abs(lse - lse_ref)) <= BF16_ATOL
+        r = bars.decode_bf16(o, lse, o_ref, lse_ref)
+        say("  " + bars.report(r))
+        assert r["ok"], r
 
 
 def _inputs(B, T, Hq, Hkv, D, dtype, seed, q_std=1.0):
@@ -258,27 +258,16 @@ def test_decode_mid_context_full():
         _compare(o, lse, o_ref, lse_ref, "bf16")
 
 
-def _sampled_heads(B, Hq, n, seed):
-    r = np.random.default_rng(seed)
-    pairs = {(int(r.integers(B)), int(r.integers(Hq))) for _ in range(n)}
-    pairs |= {(0, 0), (B - 1, Hq - 1)}
-    return sorted(pairs)
-
-
 @pytest.mark.slow
 def test_decode_long_context_full():
-    """B=4, T=131072, 32/8 heads, 1% of key rows scaled x8 (peaked softmax); sampled heads."""
+    """B=4, T=131072, 32/8 heads, 1% of key rows scaled x8 (peaked softmax); all 128 heads."""
     w = S.DECODE_LONG
     k, v = S.cache_kv(w)
     S.scale_key_rows_bf16(k, S.scaled_rows(w), w.notes["scale"])
     q = S.queries(w)
     o, lse = _decode(dev(q), dev(k), dev(v))
-    heads = _sampled_heads(w.B, w.Hq, 10, 3)
-    o_ref, lse_ref = O.decode_attention(q, k, v, heads=heads)
-    mask = np.zeros((w.B, w.Hq), bool)
-    for b, h in heads:
-        mask[b, h] = True
-    _compare(o, lse, o_ref, lse_ref, "bf16", mask=mask)
+    o_ref, lse_ref = O.decode_attention(q, k, v)          # every (sequence, head)
+    _compare(o, lse, o_ref, lse_ref, "bf16")
 
 
 @pytest.mark.slow
@@ -291,12 +280,8 @@ def test_decode_million_token_planted_row():
     S.plant_query_row_bf16(k, q, t_star, w.notes["plant_scale"])
     o, lse = _decode(dev(q), dev(k), dev(v))
     G = w.G
-    heads = [(0, g * G) for g in range(w.Hkv)] + [(0, 1), (0, w.Hq - 1)]
-    o_ref, lse_ref = O.decode_attention(q, k, v, heads=heads)
-    mask = np.zeros((w.B, w.Hq), bool)
-    for b, h in heads:
-        mask[b, h] = True
-    _compare(o, lse, o_ref, lse_ref, "bf16", mask=mask)
+    o_ref, lse_ref = O.decode_attention(q, k, v)          # all 16 heads
+    _compare(o, lse, o_ref, lse_ref, "bf16")
     for g in range(w.Hkv):
         planted = O.to_f64(v[0, g, t_star])
         say(f"  head {g * G}: max|o - V[t*]| = {np.max(np.abs(o[0, g * G] - planted)):.3e}")

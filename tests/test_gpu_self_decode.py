@@ -5,7 +5,8 @@ Bars: the row written into the cache within the compose bars (bf16: one ulp
 of the exact value plus 1e-6 of the summed terms; fp32: 1e-6 of the summed
 terms) and bit for bit what yoco_compose_kv writes; every other cache row
 untouched. The output within the decode bars (fp32 caches: per (b, h) row
-1e-5 ||o_ref||_inf; bf16: 1e-2 absolute, lse likewise) plus the first-order
+1e-5 ||o_ref||_inf; bf16: each row within 1e-3 of its rms, lse within 1e-4,
+as derived in tests/bars.py, and the stated 1e-2 absolute) plus the first-order
 effect of storing the new row rounded: the oracle attends over the exactly
 composed row, the kernel (like any later step) over the stored one, and when
 that row carries most of the softmax weight its bf16 rounding alone moves the
@@ -17,6 +18,7 @@ import torch
 import cross_layer_shared_amd as Y
 import oracle as O
 from synthetic import inputs as S
+from tests import bars
 from tests.gpu_util import bf16_to_f64, bf16_ulp, dev, host, rowwise_rel, say
 
 pytestmark = pytest.mark.gpu
@@ -97,8 +99,10 @@ def _check_output(o, lse, o_ref, lse_ref, dtype, slack):
         assert np.all(err <= bar)
         assert np.all(np.abs(lse - lse_ref) <= 1e-5 * np.maximum(1.0, np.abs(lse_ref)) + sl)
     else:
-        assert np.all(err <= 1e-2 + so)
-        assert np.all(np.abs(lse - lse_ref) <= 1e-2 + sl)
+        # the decode bars (tests/bars.py) plus the slack of the rounded new row
+        bar = bars.DECODE_REL * bars.row_rms(o_ref)[..., None] + bars.O_FLOOR + so
+        assert np.all(err <= bar) and np.all(err <= bars.STATED_ATOL + so)
+        assert np.all(np.abs(lse - lse_ref) <= bars.DECODE_LSE + sl)
 
 
 def _check_rows(k0, v0, k1, v1, new, alpha, seq_lens, dtype):
