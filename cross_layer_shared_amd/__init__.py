@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     yoco_compose_kv_backward,
     yoco_cross_attn_decode,
     yoco_cross_attn_decode_compose_on_read,
+    yoco_cross_attn_decode_noalloc,
     yoco_cross_attn_decode_partial,
     yoco_cross_attn_prefill,
     yoco_decode_merge,

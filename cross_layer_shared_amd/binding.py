@@ -20,7 +20,7 @@ YOCO_OK, YOCO_ERR_INVALID_ARG, YOCO_ERR_UNSUPPORTED, YOCO_ERR_ALIGNMENT, YOCO_ER
 YOCO_F32, YOCO_BF16 = 0, 1
 
 EXPORTED = ("yoco_compose_kv", "yoco_compose_backward_workspace_size", "yoco_compose_kv_backward", "yoco_decode_num_splits", "yoco_decode_workspace_size", "yoco_cross_attn_decode",
-            "yoco_cross_attn_decode_compose_on_read", "yoco_self_attn_decode", "yoco_cross_attn_decode_partial", "yoco_decode_merge", "yoco_cross_attn_prefill", "yoco_status_string",
+            "yoco_cross_attn_decode_noalloc", "yoco_cross_attn_decode_compose_on_read", "yoco_self_attn_decode", "yoco_cross_attn_decode_partial", "yoco_decode_merge", "yoco_cross_attn_prefill", "yoco_status_string",
             "yoco_last_error", "yoco_version")
 
 
@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.yoco_decode_workspace_size.restype = sz
     lib.yoco_cross_attn_decode.argtypes = [vp, T4, T4, vp, i, i, i, i, i, f, vp, vp, vp, sz, i, i, vp]
     lib.yoco_cross_attn_decode.restype = st
+    lib.yoco_cross_attn_decode_noalloc.argtypes = [vp, T4, T4, vp, i, i, i, i, i, f, vp, vp, i, i, vp]
+    lib.yoco_cross_attn_decode_noalloc.restype = st
     lib.yoco_cross_attn_decode_compose_on_read.argtypes = [vp, T4, T4, T4, T4, vp, i, i, i, i, i, f, f, f, f, f, f,
                                                            vp, vp, vp, sz, i, i, vp]
     lib.yoco_cross_attn_decode_compose_on_read.restype = st
@@ -213,6 +215,22 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T:
                                       out.data_ptr(), _ptr(lse), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), int(num_splits),
                                       _dtype_code(q), _stream(stream)))
+
+
+def yoco_cross_attn_decode_noalloc(q, k_cache, v_cache, out, lse=None, seq_lens=None, T: int | None = None,
+                                   num_splits: int = 0, scale: float = 0.0, stream=None,
+                                   Hkv: int | None = None) -> None:
+    """yoco_cross_attn_decode without a workspace: the partials and merge counters
+    live in the library's per-GPU scratch array (no allocation anywhere)."""
+    lib = load_library()
+    _need_contiguous(q=q, out=out, lse=lse, seq_lens=seq_lens)
+    B, Hq, D = q.shape
+    kc, vc = _as_t4(k_cache), _as_t4(v_cache)
+    Hkv = _heads(k_cache, Hkv)
+    T = kc.rows if T is None else T
+    _check(lib.yoco_cross_attn_decode_noalloc(q.data_ptr(), kc, vc, _ptr(seq_lens), B, T, Hq, Hkv, D, float(scale),
+                                              out.data_ptr(), _ptr(lse), int(num_splits), _dtype_code(q),
+                                              _stream(stream)))
 
 
 def yoco_cross_attn_decode_compose_on_read(q, k1_cache, ki_cache, v1_cache, vi_cache, alpha, out, lse=None,

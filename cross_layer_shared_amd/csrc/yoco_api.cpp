@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/yoco.h"
 #include "common.h"
@@ -109,6 +110,51 @@ yoco_status check_decode(const void* q, const yoco_tensor4& k, const yoco_tensor
   if ((st = check_tensor("v_cache", v, T, es)) != YOCO_OK) return st;
   if ((st = check_head_span("k_cache", k, T, es)) != YOCO_OK) return st;
   if ((st = check_head_span("v_cache", v, T, es)) != YOCO_OK) return st;
+  return YOCO_OK;
+}
+
+// ---- scratch memory of the allocation-free decode (yoco_cross_attn_decode_noalloc) ----
+// One array per GPU, held until the process ends: the merge counters in a
+// fixed leading section (so that they never share bytes with the partials of
+// a call with a different shape), then the split partials. In host code
+// `scratch` only names the symbol; its device address on the current GPU is
+// looked up once per device (scratch_on_device) and only that address is used.
+constexpr size_t kScratchBytes = YOCO_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchCounterBytes = YOCO_NOALLOC_COUNTER_BYTES;
+static_assert(kScratchCounterBytes % 256 == 0 && kScratchCounterBytes < kScratchBytes, "scratch layout");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};
+
+// Device address of the scratch array on the current GPU. The first call on a
+// device looks it up and clears the counter section with a kernel on `stream`
+// (every completed decode leaves its counters at zero again).
+yoco_status scratch_on_device(hipStream_t stream, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(YOCO_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(YOCO_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(YOCO_ERR_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int words = (int)(kScratchCounterBytes / 4);
+    zero_words<<<(words + 255) / 256, 256, 0, stream>>>(static_cast<uint32_t*>(ptr), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(YOCO_ERR_LAUNCH, "clearing the scratch counters: %s", hipGetErrorString(e));
+    g_scratch[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch[dev];
   return YOCO_OK;
 }
 
@@ -334,9 +380,12 @@ size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_
   return ws_layout(B, Hq, Hkv, D, S).total;
 }
 
+// Checks and launch parameters of a decode call. With attach_workspace the
+// partials are placed in the caller's workspace (when the split count is above
+// one); otherwise the caller places them.
 static yoco_status decode_setup(const void* q, yoco_tensor4 k, yoco_tensor4 v, const int32_t* seq_lens, int B, int T,
                                 int Hq, int Hkv, int D, float scale, void* workspace, size_t ws_bytes, int S,
-                                yoco_dtype dt, yoco::DecodeParams* p) {
+                                yoco_dtype dt, yoco::DecodeParams* p, bool attach_workspace = true) {
   yoco_status st = check_decode(q, k, v, B, T, Hq, Hkv, D, dt);
   if (st != YOCO_OK) return st;
   if (S < 1) return fail(YOCO_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", S);
@@ -371,7 +420,7 @@ static yoco_status decode_setup(const void* q, yoco_tensor4 k, yoco_tensor4 v, c
   p->nk1 = p->nki = p->nv1 = p->nvi = yoco::View4{nullptr, 0, 0, 0};
   p->cK1 = p->cK2 = p->cV1 = p->cV2 = 0.f;
   p->termsK = p->termsV = 0;
-  if (S > 1) {
+  if (S > 1 && attach_workspace) {
     WsLayout w = ws_layout(B, Hq, Hkv, D, S);
     if (!workspace) return fail(YOCO_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
     if (ws_bytes < w.total) return fail(YOCO_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, w.total);
@@ -404,6 +453,42 @@ yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_ten
     p.tickets = static_cast<unsigned*>(workspace);
   }
   return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode");
+}
+
+yoco_status yoco_cross_attn_decode_noalloc(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
+                                           const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D, float scale,
+                                           float* out, float* lse, int num_splits, yoco_dtype kv_dtype,
+                                           hipStream_t stream) {
+  if (num_splits < 0) return fail(YOCO_ERR_INVALID_ARG, "num_splits must be >= 0");
+  int S = num_splits ? num_splits : yoco_decode_num_splits(B, T, Hq, Hkv, D);
+  if (S == 0) return fail(YOCO_ERR_INVALID_ARG, "sizes must be positive");
+  yoco::DecodeParams p;
+  yoco_status st = decode_setup(q, k_cache, v_cache, seq_lens, B, T, Hq, Hkv, D, scale, nullptr, 0, S, kv_dtype, &p,
+                                /*attach_workspace=*/false);
+  if (st != YOCO_OK) return st;
+  if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
+  if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
+  p.out = out;
+  p.lse = lse;
+  if (S > 1) {
+    // counters in the fixed leading section, then part_o and part_lse (16-byte aligned)
+    const size_t rows = (size_t)B * Hq * S;
+    const size_t o_bytes = rows * D * sizeof(float);
+    const size_t need = kScratchCounterBytes + o_bytes + (size_t)round_up((int64_t)(rows * sizeof(float)), 16);
+    if ((size_t)B * Hkv * 4 > kScratchCounterBytes)
+      return fail(YOCO_ERR_WORKSPACE, "B*Hkv = %lld exceeds the %zu merge counters of the scratch array",
+                  (long long)B * Hkv, kScratchCounterBytes / 4);
+    if (need > kScratchBytes)
+      return fail(YOCO_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the scratch array holds %zu", need,
+                  kScratchBytes);
+    char* base = nullptr;
+    if ((st = scratch_on_device(stream, &base)) != YOCO_OK) return st;
+    p.tickets = reinterpret_cast<unsigned*>(base);
+    p.part_o = reinterpret_cast<float*>(base + kScratchCounterBytes);
+    p.part_lse = reinterpret_cast<float*>(base + kScratchCounterBytes + o_bytes);
+  }
+  return launched(yoco::launch_decode_partial(p, kv_dtype == YOCO_BF16, stream), "decode (no allocation)");
 }
 
 yoco_status yoco_cross_attn_decode_compose_on_read(const void* q, yoco_tensor4 k1_cache, yoco_tensor4 ki_cache,

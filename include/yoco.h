@@ -18,8 +18,9 @@
  *     device, unless stated otherwise. The caller owns every buffer (inputs,
  *     caches, outputs, workspace). The library never allocates, frees or
  *     synchronises; kernels are enqueued asynchronously on `stream` (NULL is
- *     the null stream). Functions keep no state between calls and may be
- *     called from several host threads.
+ *     the null stream). Functions keep no state between calls (the one
+ *     exception is the per-GPU scratch array of yoco_cross_attn_decode_noalloc)
+ *     and may be called from several host threads.
  *   - Every argument is checked before anything is enqueued. On error the
  *     function returns a non-zero yoco_status, enqueues nothing and records
  *     a message readable with yoco_last_error() on the same host thread.
@@ -190,6 +191,32 @@ yoco_status yoco_cross_attn_decode(const void* q, yoco_tensor4 k_cache, yoco_ten
                                    float scale, float* out, float* lse, void* workspace,
                                    size_t workspace_bytes, int num_splits, yoco_dtype kv_dtype,
                                    hipStream_t stream);
+
+/*
+ * yoco_cross_attn_decode_noalloc - yoco_cross_attn_decode with no workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The split partials and the merge counters live in a scratch array inside
+ * the library: YOCO_NOALLOC_SCRATCH_BYTES bytes of device memory per GPU that
+ * runs it, held until the process ends; the first YOCO_NOALLOC_COUNTER_BYTES
+ * hold the counters (so B * Hkv <= YOCO_NOALLOC_COUNTER_BYTES / 4), the rest
+ * the partials, 4 * B * Hq * S * (D + 1) bytes (16-byte aligned sections). A
+ * call that needs more returns YOCO_ERR_WORKSPACE and enqueues nothing; a call
+ * whose effective split count is 1 uses no scratch. Nothing is allocated or
+ * freed. The first call on a device looks up the array's address and clears
+ * its counters with a kernel on `stream`: make that call outside graph capture.
+ * Every call on one GPU shares that GPU's array, and every completed call
+ * leaves the counters at zero: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be ordered by the caller.
+ * Arguments, results and the other errors as for yoco_cross_attn_decode.
+ */
+#define YOCO_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define YOCO_NOALLOC_COUNTER_BYTES (64u << 10)
+yoco_status yoco_cross_attn_decode_noalloc(const void* q, yoco_tensor4 k_cache, yoco_tensor4 v_cache,
+                                           const int32_t* seq_lens, int B, int T, int Hq, int Hkv, int D,
+                                           float scale, float* out, float* lse, int num_splits,
+                                           yoco_dtype kv_dtype, hipStream_t stream);
 
 /*
  * yoco_cross_attn_decode_compose_on_read - the same decode when the cache holds

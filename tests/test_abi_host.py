@@ -292,3 +292,22 @@ def test_ceiling_probes_reject_bad_arguments():
     for got, want in cases:
         assert got == want
         assert lib.yoco_ceiling_last_error().decode()
+
+
+def test_noalloc_decode_rejects_before_any_launch(lib):
+    """The allocation-free decode checks its arguments like the workspace decode,
+    and rejects calls whose partials or counters exceed its scratch array."""
+    def call(B=8, T=4096, Hq=32, Hkv=8, D=128, S=0, q=BASE, out=BASE + (1 << 30), dt=BF16):
+        k = t4(BASE + (2 << 30), sb=Hkv * T * D, sh=T * D, st=D, rows=T)
+        v = t4(BASE + (3 << 30), sb=Hkv * T * D, sh=T * D, st=D, rows=T)
+        return lib.yoco_cross_attn_decode_noalloc(q, k, v, None, B, T, Hq, Hkv, D, 0.0, out, None, S, dt, None)
+    assert call(B=0) == INVALID
+    assert call(q=0) == INVALID
+    assert call(out=BASE + 4) == ALIGN
+    assert call(D=96) == UNSUPPORTED
+    assert call(S=-1) == INVALID
+    assert call(T=100, S=101) == INVALID
+    assert call(B=64, Hq=64, Hkv=64, T=64, S=16) == WORKSPACE            # partials beyond 8 MiB
+    assert "scratch" in Y.yoco_last_error()
+    assert call(B=4096, Hq=8, Hkv=8, T=64, S=2) == WORKSPACE             # 32768 counters > 16384
+    assert "counters" in Y.yoco_last_error()
