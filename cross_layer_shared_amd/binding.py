@@ -114,6 +114,10 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _bytes(t: torch.Tensor | None) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def token_major(t: torch.Tensor) -> Tensor4:
     """[B, n, H, D] (D contiguous) -> Tensor4 with t as the token axis."""
     if t.dim() != 4 or t.stride(3) != 1:
@@ -174,8 +178,8 @@ def yoco_compose_kv_backward(gk, gv, t0: int, k1, ki, v1, vi, dk1, dki, dv1, dvi
     B, n, Hkv, D = k1.shape
     dtype = _dtype_code(k1)
     if workspace is None:
-        nbytes = max(16, yoco_compose_backward_workspace_size(B, n, Hkv, D, dtype))
-        workspace = torch.empty(math.ceil(nbytes / 16) * 4, dtype=torch.float32, device=k1.device)
+        workspace = _cached_workspace("compose_backward", yoco_compose_backward_workspace_size(B, n, Hkv, D, dtype),
+                                      k1.device, stream)
     srcs = [token_major(x) for x in (k1, ki, v1, vi)]
     grads = [token_major(x) for x in (dk1, dki, dv1, dvi)]
     aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
@@ -199,6 +203,52 @@ def decode_workspace(B, T, Hq, Hkv, D, num_splits=0, device="cuda") -> torch.Ten
     return torch.zeros(math.ceil(nbytes / 16) * 4, dtype=torch.float32, device=device)
 
 
+def _torch_stream(stream, device):
+    """The torch stream object for a binding `stream` argument (None: the current one)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+# Workspaces the binding keeps for calls that pass none: one per (device, stream,
+# kind), so that calls on one stream (which run in order) share it and calls on
+# different streams never do. An entry is [tensor, counters]: `counters` is the
+# B * Hkv of the last decode that used it, whose counter section that call left
+# at zero.
+_WORKSPACES: dict = {}
+
+
+def _cached_workspace(kind: str, nbytes: int, device, stream, counters: int = 0) -> torch.Tensor | None:
+    """The binding's own workspace of at least nbytes for a call on (device, stream).
+
+    Allocated zero-filled (on the call's stream) the first time and whenever a
+    call needs more bytes than the one held; otherwise reused without any
+    allocation. For the decode (kind "decode"), when this call has more merge
+    counters than the last one, the bytes between the two counter sections
+    (which held the last call's partials) are zeroed first on the call's stream.
+    Pass a workspace explicitly under HIP graph capture."""
+    if nbytes == 0:                          # no workspace used: the held one keeps its state
+        return None
+    ts = _torch_stream(stream, device)
+    key = (torch.device(device).index, ts.cuda_stream, kind)
+    entry = _WORKSPACES.get(key)
+    with torch.cuda.stream(ts):
+        if entry is None or entry[0].numel() * 4 < nbytes:
+            entry = [torch.zeros(math.ceil(max(16, nbytes) / 16) * 4, dtype=torch.float32, device=device), 0]
+            _WORKSPACES[key] = entry
+        elif counters > entry[1]:
+            entry[0][entry[1]:counters].zero_()     # 4-byte counters: one float32 slot each
+        entry[1] = max(counters, 0)
+    return entry[0]
+
+
+def _decode_workspace_for(B, T, Hq, Hkv, D, num_splits, device, stream) -> torch.Tensor | None:
+    nbytes = yoco_decode_workspace_size(B, T, Hq, Hkv, D, num_splits)
+    return _cached_workspace("decode", nbytes, device, stream, counters=B * Hkv)
+
+
 def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T: int | None = None,
                            num_splits: int = 0, workspace: torch.Tensor | None = None, scale: float = 0.0,
                            stream=None, Hkv: int | None = None) -> None:
@@ -210,10 +260,9 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, out, lse=None, seq_lens=None, T:
     Hkv = _heads(k_cache, Hkv)
     T = kc.rows if T is None else T
     if workspace is None:
-        workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
+        workspace = _decode_workspace_for(B, T, Hq, Hkv, D, num_splits, q.device, stream)
     _check(lib.yoco_cross_attn_decode(q.data_ptr(), kc, vc, _ptr(seq_lens), B, T, Hq, Hkv, D, float(scale),
-                                      out.data_ptr(), _ptr(lse), workspace.data_ptr(),
-                                      workspace.numel() * workspace.element_size(), int(num_splits),
+                                      out.data_ptr(), _ptr(lse), _ptr(workspace), _bytes(workspace), int(num_splits),
                                       _dtype_code(q), _stream(stream)))
 
 
@@ -245,11 +294,11 @@ def yoco_cross_attn_decode_compose_on_read(q, k1_cache, ki_cache, v1_cache, vi_c
     Hkv = _heads(ki_cache, Hkv)
     T = ki.rows if T is None else T
     if workspace is None:
-        workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
+        workspace = _decode_workspace_for(B, T, Hq, Hkv, D, num_splits, q.device, stream)
     aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
     _check(lib.yoco_cross_attn_decode_compose_on_read(
         q.data_ptr(), k1, ki, v1, vi, _ptr(seq_lens), B, T, Hq, Hkv, D, float(lam), aK1, aK2, aV1, aV2, float(scale),
-        out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), _ptr(lse), _ptr(workspace), _bytes(workspace),
         int(num_splits), _dtype_code(q), _stream(stream)))
 
 
@@ -281,11 +330,11 @@ def yoco_self_attn_decode(q, k1_new, ki_new, v1_new, vi_new, k_cache, v_cache, a
     Hkv = _heads(k_cache, Hkv)
     T = kc.rows if T is None else T
     if workspace is None:
-        workspace = decode_workspace(B, T, Hq, Hkv, D, num_splits, q.device)
+        workspace = _decode_workspace_for(B, T, Hq, Hkv, D, num_splits, q.device, stream)
     aK1, aK2, aV1, aV2 = (float(a) for a in alpha)
     _check(lib.yoco_self_attn_decode(
         q.data_ptr(), *srcs, kc, vc, _ptr(seq_lens), B, T, Hq, Hkv, D, float(lam), aK1, aK2, aV1, aV2,
-        float(scale), out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        float(scale), out.data_ptr(), _ptr(lse), _ptr(workspace), _bytes(workspace),
         int(num_splits), _dtype_code(q), _stream(stream)))
 
 

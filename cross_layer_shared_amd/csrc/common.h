@@ -1,7 +1,9 @@
-// Shared host/device definitions of the gfx950 HIP path (no oracle code here).
+// Shared host-side definitions of the gfx950 HIP path: launch parameters and
+// launcher declarations (no oracle code here). Host code only, so that the C
+// ABI layer builds with any C++ compiler.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace yoco {
@@ -23,6 +25,10 @@ struct ComposeParams {
 };
 hipError_t launch_compose(const ComposeParams& p, bool bf16, hipStream_t stream);
 
+// Which terms of a composition are present: 3 = both, 2 = only X_i, 1 = only
+// X_1, 0 = none (a zero coefficient drops its term and its read).
+inline int compose_terms(float c1, float c2) { return (c1 != 0.f ? 1 : 0) | (c2 != 0.f ? 2 : 0); }
+
 struct ComposeBackwardParams {
   View4 gk, gv;              // upstream gradients of K', V' (rows [t0, t0 + n)), cache dtype
   View4 k1, ki, v1, vi;      // forward sources (rows [0, n)), cache dtype
@@ -32,7 +38,14 @@ struct ComposeBackwardParams {
   float lambda;
   float* dalpha;             // [4] fp32: daK1, daK2, daV1, daV2
 };
-int compose_backward_blocks(const ComposeBackwardParams& p, bool bf16);
+// Launch shape of the backward: kBackwardThreads threads per workgroup, each
+// handling kBackwardVecPerThread four-element vectors.
+constexpr int kBackwardThreads = 256;
+constexpr int kBackwardVecPerThread = 4;
+inline int compose_backward_blocks(const ComposeBackwardParams& p) {
+  const uint64_t total = (uint64_t)p.B * p.n * p.Hkv * (p.D / 4);
+  return (int)((total + kBackwardThreads * kBackwardVecPerThread - 1) / (kBackwardThreads * kBackwardVecPerThread));
+}
 hipError_t launch_compose_backward(const ComposeBackwardParams& p, bool bf16, float* partial, hipStream_t stream);
 
 struct DecodeParams {
@@ -76,5 +89,11 @@ struct PrefillParams {
   float* lse;      // [B, Hq, C] or null
 };
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+// Device address of the allocation-free decode's scratch array on the current
+// GPU (YOCO_NOALLOC_SCRATCH_BYTES bytes, the first YOCO_NOALLOC_COUNTER_BYTES
+// of them merge counters). The first call on a device looks it up and clears
+// the counters with a kernel on `stream`.
+hipError_t noalloc_scratch(hipStream_t stream, char** ptr);
 
 }  // namespace yoco

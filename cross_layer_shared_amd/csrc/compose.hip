@@ -12,6 +12,8 @@
 // runtime-invariant sizes, each done with one high multiply (+1-2% measured
 // over the compiler's generic 32-bit division).
 
+#include <hip/hip_runtime.h>
+
 #include "common.h"
 #include "compose_math.h"
 #include "fastdiv.h"

@@ -18,6 +18,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_runtime.h>
+
 #include "common.h"
 #include "compose_math.h"
 #include "fastdiv.h"
@@ -25,8 +27,8 @@
 namespace yoco {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;   // four-element vectors per thread, loads issued together
+constexpr int kThreads = kBackwardThreads;
+constexpr int kVecPerThread = kBackwardVecPerThread;   // four-element vectors per thread, loads issued together
 constexpr int kFinishThreads = 1024;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -184,16 +186,10 @@ __global__ __launch_bounds__(kFinishThreads) void compose_backward_finish(const 
 
 }  // namespace
 
-int compose_backward_blocks(const ComposeBackwardParams& p, bool bf16) {
-  (void)bf16;
-  const uint64_t total = (uint64_t)p.B * p.n * p.Hkv * (p.D / 4);
-  return (int)((total + kThreads * kVecPerThread - 1) / (kThreads * kVecPerThread));
-}
-
 hipError_t launch_compose_backward(const ComposeBackwardParams& p, bool bf16, float* partial, hipStream_t stream) {
   const uint32_t cpr = (uint32_t)(p.D / 4);
   const uint32_t total = (uint32_t)((uint64_t)p.B * p.n * p.Hkv * cpr);
-  const int nb = compose_backward_blocks(p, bf16);
+  const int nb = compose_backward_blocks(p);
   const FastDiv dc = make_fastdiv(cpr), dh = make_fastdiv((uint32_t)p.Hkv), dn = make_fastdiv((uint32_t)p.n);
   if (bf16)
     compose_backward_kernel<true><<<nb, kThreads, 0, stream>>>(p, cpr, total, dc, dh, dn, partial);

@@ -13,10 +13,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace yoco {
+#include "common.h"
 
-// Which terms are present: 3 = both, 2 = only X_i, 1 = only X_1, 0 = none.
-inline int compose_terms(float c1, float c2) { return (c1 != 0.f ? 1 : 0) | (c2 != 0.f ? 2 : 0); }
+namespace yoco {
 
 __device__ __forceinline__ float compose_value(float x1, float xi, float c1, float c2, int terms) {
   switch (terms) {

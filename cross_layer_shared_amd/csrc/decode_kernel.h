@@ -54,6 +54,8 @@
 
 #include <math.h>
 
+#include <hip/hip_runtime.h>
+
 #include "common.h"
 #include "compose_math.h"
 

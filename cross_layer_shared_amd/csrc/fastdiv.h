@@ -21,9 +21,9 @@ inline FastDiv make_fastdiv(uint32_t d) {
   const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
   return {d, (uint32_t)m, s};
 }
-__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
   if (f.s == 0) return x;
-  const uint32_t t = __umulhi(x, f.m);
+  const uint32_t t = (uint32_t)(((uint64_t)x * f.m) >> 32);   // high word of the product (v_mul_hi_u32)
   return (t + ((x - t) >> 1)) >> (f.s - 1);
 }
 

@@ -42,6 +42,8 @@
 
 #include <math.h>
 
+#include <hip/hip_runtime.h>
+
 #include "common.h"
 
 namespace yoco {

@@ -8,11 +8,9 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "../../include/yoco.h"
 #include "common.h"
-#include "compose_math.h"
 
 namespace {
 
@@ -65,6 +63,34 @@ yoco_status check_tensor(const char* name, const yoco_tensor4& t, int64_t rows_n
   return YOCO_OK;
 }
 
+// Rows of one (sequence, head) must not overlap: a cache read row by row, or a
+// tensor written row by row, needs stride_t >= D (a stride of 0 would make
+// every row the same memory).
+yoco_status check_row_stride(const char* name, const yoco_tensor4& t, int D) {
+  if (t.stride_t < D)
+    return fail(YOCO_ERR_INVALID_ARG, "%s: stride_t = %lld is below D = %d (rows overlap)", name,
+                (long long)t.stride_t, D);
+  return YOCO_OK;
+}
+
+// A tensor the kernels write must give every element (b, h, t, d) of its B x H x
+// rows x D extent an address of its own: sorted by stride, each axis of extent
+// above one must step past the whole span of the axes below it.
+yoco_status check_distinct(const char* name, const yoco_tensor4& t, int B, int H, int64_t rows, int D) {
+  struct Axis {
+    int64_t stride, extent;
+  } ax[4] = {{1, D}, {t.stride_t, rows}, {t.stride_h, H}, {t.stride_b, B}};
+  std::sort(ax, ax + 4, [](const Axis& a, const Axis& b) { return a.stride < b.stride; });
+  int64_t span = 0;   // elements spanned by the axes taken so far, minus one
+  for (const Axis& a : ax) {
+    if (a.extent <= 1) continue;
+    if (a.stride <= span)
+      return fail(YOCO_ERR_INVALID_ARG, "%s: strides map two elements to one address", name);
+    span += a.stride * (a.extent - 1);
+  }
+  return YOCO_OK;
+}
+
 // The decode kernels address one (sequence, head)'s rows with 32-bit byte
 // offsets: rows [0, T) plus one block of overrun must span less than 2 GiB.
 yoco_status check_head_span(const char* name, const yoco_tensor4& t, int64_t T, size_t es) {
@@ -108,55 +134,18 @@ yoco_status check_decode(const void* q, const yoco_tensor4& k, const yoco_tensor
   yoco_status st;
   if ((st = check_tensor("k_cache", k, T, es)) != YOCO_OK) return st;
   if ((st = check_tensor("v_cache", v, T, es)) != YOCO_OK) return st;
+  if ((st = check_row_stride("k_cache", k, D)) != YOCO_OK) return st;
+  if ((st = check_row_stride("v_cache", v, D)) != YOCO_OK) return st;
   if ((st = check_head_span("k_cache", k, T, es)) != YOCO_OK) return st;
   if ((st = check_head_span("v_cache", v, T, es)) != YOCO_OK) return st;
   return YOCO_OK;
 }
 
-// ---- scratch memory of the allocation-free decode (yoco_cross_attn_decode_noalloc) ----
-// One array per GPU, held until the process ends: the merge counters in a
-// fixed leading section (so that they never share bytes with the partials of
-// a call with a different shape), then the split partials. In host code
-// `scratch` only names the symbol; its device address on the current GPU is
-// looked up once per device (scratch_on_device) and only that address is used.
+// Layout of the allocation-free decode's scratch array (decode_noalloc.hip):
+// the merge counters in a fixed leading section, so that they never share
+// bytes with the partials of a call with a different shape, then the partials.
 constexpr size_t kScratchBytes = YOCO_NOALLOC_SCRATCH_BYTES;
 constexpr size_t kScratchCounterBytes = YOCO_NOALLOC_COUNTER_BYTES;
-static_assert(kScratchCounterBytes % 256 == 0 && kScratchCounterBytes < kScratchBytes, "scratch layout");
-
-static __device__ __align__(256) unsigned char scratch[kScratchBytes];
-
-__global__ void zero_words(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-char* g_scratch[kMaxDevices] = {};
-
-// Device address of the scratch array on the current GPU. The first call on a
-// device looks it up and clears the counter section with a kernel on `stream`
-// (every completed decode leaves its counters at zero again).
-yoco_status scratch_on_device(hipStream_t stream, char** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(YOCO_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= kMaxDevices) return fail(YOCO_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch[dev]) {
-    void* ptr = nullptr;
-    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
-    if (e != hipSuccess || !ptr)
-      return fail(YOCO_ERR_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
-    const int words = (int)(kScratchCounterBytes / 4);
-    zero_words<<<(words + 255) / 256, 256, 0, stream>>>(static_cast<uint32_t*>(ptr), words);
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(YOCO_ERR_LAUNCH, "clearing the scratch counters: %s", hipGetErrorString(e));
-    g_scratch[dev] = static_cast<char*>(ptr);
-  }
-  *out = g_scratch[dev];
-  return YOCO_OK;
-}
 
 }  // namespace
 
@@ -199,6 +188,8 @@ yoco_status yoco_compose_kv(yoco_tensor4 k1, yoco_tensor4 ki, yoco_tensor4 v1, y
     int64_t need = i < 4 ? (int64_t)n : (int64_t)t0 + n;
     if ((st = check_tensor(names[i], *ts[i], need, es)) != YOCO_OK) return st;
   }
+  if ((st = check_distinct("k_cache", k_cache, B, Hkv, n, D)) != YOCO_OK) return st;
+  if ((st = check_distinct("v_cache", v_cache, B, Hkv, n, D)) != YOCO_OK) return st;
   // Overlap rules: a source may alias a destination exactly (in-place, t0 = 0);
   // any other overlap of a source with a destination is rejected, and so is
   // k_cache overlapping v_cache with the same layout.
@@ -276,7 +267,7 @@ size_t yoco_compose_backward_workspace_size(int B, int n, int Hkv, int D, yoco_d
   p.n = n;
   p.Hkv = Hkv;
   p.D = D;
-  return (size_t)yoco::compose_backward_blocks(p, dtype == YOCO_BF16) * 4 * sizeof(float);
+  return (size_t)yoco::compose_backward_blocks(p) * 4 * sizeof(float);
 }
 
 yoco_status yoco_compose_kv_backward(yoco_tensor4 gk, yoco_tensor4 gv, int t0, yoco_tensor4 k1, yoco_tensor4 ki,
@@ -305,7 +296,9 @@ yoco_status yoco_compose_kv_backward(yoco_tensor4 gk, yoco_tensor4 gv, int t0, y
   const char* out_names[4] = {"dk1", "dki", "dv1", "dvi"};
   const yoco_tensor4* outs[4] = {&dk1, &dki, &dv1, &dvi};
   for (int i = 0; i < 4; ++i)
-    if ((st = check_tensor(out_names[i], *outs[i], n, 4)) != YOCO_OK) return st;
+    if ((st = check_tensor(out_names[i], *outs[i], n, 4)) != YOCO_OK ||
+        (st = check_distinct(out_names[i], *outs[i], B, Hkv, n, D)) != YOCO_OK)
+      return st;
   // the four gradient outputs must not overlap one another or any input
   for (int i = 0; i < 4; ++i) {
     Span so = span_of(*outs[i], B, Hkv, 0, n, D, 4);
@@ -483,7 +476,8 @@ yoco_status yoco_cross_attn_decode_noalloc(const void* q, yoco_tensor4 k_cache, 
       return fail(YOCO_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the scratch array holds %zu", need,
                   kScratchBytes);
     char* base = nullptr;
-    if ((st = scratch_on_device(stream, &base)) != YOCO_OK) return st;
+    const hipError_t e = yoco::noalloc_scratch(stream, &base);
+    if (e != hipSuccess) return fail(YOCO_ERR_LAUNCH, "scratch array: %s", hipGetErrorString(e));
     p.tickets = reinterpret_cast<unsigned*>(base);
     p.part_o = reinterpret_cast<float*>(base + kScratchCounterBytes);
     p.part_lse = reinterpret_cast<float*>(base + kScratchCounterBytes + o_bytes);
@@ -508,6 +502,8 @@ yoco_status yoco_cross_attn_decode_compose_on_read(const void* q, yoco_tensor4 k
   const size_t es = esize(kv_dtype);
   if ((st = check_tensor("k1_cache", k1_cache, T, es)) != YOCO_OK) return st;
   if ((st = check_tensor("v1_cache", v1_cache, T, es)) != YOCO_OK) return st;
+  if ((st = check_row_stride("k1_cache", k1_cache, D)) != YOCO_OK) return st;
+  if ((st = check_row_stride("v1_cache", v1_cache, D)) != YOCO_OK) return st;
   if ((st = check_head_span("k1_cache", k1_cache, T, es)) != YOCO_OK) return st;
   if ((st = check_head_span("v1_cache", v1_cache, T, es)) != YOCO_OK) return st;
   if (!isfinite(lambda) || !isfinite(aK1) || !isfinite(aK2) || !isfinite(aV1) || !isfinite(aV2))
@@ -567,6 +563,9 @@ yoco_status yoco_self_attn_decode(const void* q, yoco_tensor4 k1_new, yoco_tenso
   }
   if (overlap(span_of(k_cache, B, Hkv, 0, T, D, es), span_of(v_cache, B, Hkv, 0, T, D, es)))
     return fail(YOCO_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+  // each (sequence, kv head) writes its own row n - 1
+  if ((st = check_distinct("k_cache", k_cache, B, Hkv, T, D)) != YOCO_OK) return st;
+  if ((st = check_distinct("v_cache", v_cache, B, Hkv, T, D)) != YOCO_OK) return st;
   if (!out) return fail(YOCO_ERR_INVALID_ARG, "out: null pointer");
   if (!aligned16(out)) return fail(YOCO_ERR_ALIGNMENT, "out: not 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "lse: not 4-byte aligned");
@@ -641,6 +640,8 @@ yoco_status yoco_cross_attn_prefill(const void* q, yoco_tensor4 k_cache, yoco_te
   int64_t need = (int64_t)p0 + C;
   if ((st = check_tensor("k_cache", k_cache, need, 2)) != YOCO_OK) return st;
   if ((st = check_tensor("v_cache", v_cache, need, 2)) != YOCO_OK) return st;
+  if ((st = check_row_stride("k_cache", k_cache, D)) != YOCO_OK) return st;
+  if ((st = check_row_stride("v_cache", v_cache, D)) != YOCO_OK) return st;
   if (need > INT32_MAX / 2) return fail(YOCO_ERR_UNSUPPORTED, "cache too long");
   if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)D);
   if (!isfinite(scale)) return fail(YOCO_ERR_INVALID_ARG, "scale must be finite");

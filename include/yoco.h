@@ -28,7 +28,13 @@
  *   - A 4-D tensor is described by yoco_tensor4: element strides for the
  *     batch, head and token axes; the head-dimension axis (D) is contiguous.
  *     Base pointers must be 16-byte aligned and every stride times the
- *     element size a multiple of 16 bytes (YOCO_ERR_ALIGNMENT).
+ *     element size a multiple of 16 bytes (YOCO_ERR_ALIGNMENT). Strides are
+ *     non-negative. A cache that attention reads row by row needs
+ *     stride_t >= D; a tensor the library writes must give each of its
+ *     elements an address of its own (no stride 0 over an axis longer than
+ *     one, no overlapping rows); both are YOCO_ERR_INVALID_ARG otherwise.
+ *     Sources that are only read (compose inputs, the one-token rows of
+ *     yoco_self_attn_decode) may use any strides, including 0.
  *   - bf16 values are IEEE binary32 values truncated to their upper 16 bits;
  *     every result written as bf16 is rounded to nearest, ties to even.
  *   - Grouped-query attention: query head h reads kv head h / (Hq / Hkv).
@@ -173,11 +179,15 @@ size_t yoco_decode_workspace_size(int B, int T, int Hq, int Hkv, int D, int num_
  *   workspace  device buffer of at least yoco_decode_workspace_size(...) bytes,
  *              16-byte aligned; ignored (may be NULL) when the effective split
  *              count is 1. Its counter section (the first 4 * B * Hkv bytes)
- *              must be zero before the first call that uses the workspace
- *              (zero-fill the buffer once); every completed call leaves it zero
- *              again, whatever T and the split count are. One workspace serves one
- *              call at a time: calls that share a workspace must be ordered
- *              (same stream, or synchronised).
+ *              must be zero when a call starts. Zero-fill a new workspace once:
+ *              every completed call leaves its own counter section zero again,
+ *              whatever T and the split count are, but the bytes after it hold
+ *              that call's partials. So a workspace reused for a call with a
+ *              larger B * Hkv than the call before needs bytes
+ *              [4 * B_prev * Hkv_prev, 4 * B * Hkv) zeroed first (or keep one
+ *              workspace per B * Hkv). One workspace serves one call at a time:
+ *              calls that share a workspace must be ordered (same stream, or
+ *              synchronised).
  *   num_splits 0 = automatic; otherwise the split count S >= 1.
  *   kv_dtype   YOCO_F32 or YOCO_BF16; D in {64, 128}; Hq a multiple of Hkv,
  *              Hq / Hkv in {1, 2, 4, 8, 16}.

@@ -311,3 +311,38 @@ def test_noalloc_decode_rejects_before_any_launch(lib):
     assert "scratch" in Y.yoco_last_error()
     assert call(B=4096, Hq=8, Hkv=8, T=64, S=2) == WORKSPACE             # 32768 counters > 16384
     assert "counters" in Y.yoco_last_error()
+
+
+def test_overlapping_rows_and_aliased_destinations_are_rejected(lib):
+    """A cache read row by row needs stride_t >= D (stride 0 would read one row,
+    or nothing through the decode's row-bounded buffer); a tensor the library
+    writes must give every element an address of its own."""
+    # decode and prefill caches: stride_t 0 or below D
+    for st in (0, 64):
+        bad = t4(BASE + (1 << 28), rows=4096, sb=8 * 4096 * 128, sh=4096 * 128, st=st)
+        assert decode(lib, k=bad) == INVALID and "stride_t" in Y.yoco_last_error()
+        assert decode(lib, v=bad) == INVALID
+        badp = t4(BASE + (1 << 28), rows=8192, sb=8 * 8192 * 128, sh=8192 * 128, st=st)
+        assert prefill(lib, k=badp) == INVALID
+    # compose destinations: heads or sequences sharing memory
+    assert compose(lib, kc=t4(BASE + (4 << 24), sh=0)) == INVALID
+    assert "address" in Y.yoco_last_error()
+    assert compose(lib, vc=t4(BASE + (5 << 24), st=64)) == INVALID
+    assert compose(lib, B=2, kc=t4(BASE + (4 << 24), sb=0, rows=256), k1=src4(BASE, B=2), ki=src4(BASE + (1 << 24), B=2),
+                   v1=src4(BASE + (2 << 24), B=2), vi=src4(BASE + (3 << 24), B=2)) == INVALID
+
+
+def test_self_decode_and_backward_destinations_must_not_alias(lib):
+    kc = t4(BASE + (1 << 28), rows=4096, sb=8 * 4096 * 128, sh=0)        # all kv heads on one memory
+    vc = t4(BASE + (2 << 28), rows=4096, sb=8 * 4096 * 128, sh=4096 * 128)
+    one = t4(BASE + (5 << 28), sb=8 * 128, sh=128, st=0, rows=1)
+    st = lib.yoco_self_attn_decode(BASE, one, one, one, one, kc, vc, None, 8, 4096, 32, 8, 128, 35.0, 0.0, 0.02, 0.01,
+                                   0.03, 0.0, BASE + (3 << 28), None, BASE + (4 << 28), 1 << 30, 0, BF16, None)
+    assert st == INVALID
+    src = [src4(BASE + (i << 24)) for i in range(4)]
+    gk, gv = t4(BASE + (4 << 24)), t4(BASE + (5 << 24))
+    g32 = [Tensor4(BASE + ((6 + i) << 24), 256 * 8 * 128, 128, 8 * 128, 256) for i in range(4)]
+    g32[1] = Tensor4(BASE + (7 << 24), 256 * 8 * 128, 0, 8 * 128, 256)   # dki: kv heads alias
+    st = lib.yoco_compose_kv_backward(gk, gv, 0, *src, *g32, 1, 256, 8, 128, 35.0, 0.01, 0.02, 0.03, 0.04,
+                                      BASE + (12 << 24), BASE + (13 << 24), 1 << 20, BF16, None)
+    assert st == INVALID

@@ -208,6 +208,36 @@ def test_fused_merge_reuses_one_workspace():
         _compare(host(out).astype(np.float64), host(lse).astype(np.float64), o_ref, lse_ref, "bf16")
 
 
+def test_workspace_reused_for_more_counters_after_rezeroing():
+    """A call with one (sequence, kv head) leaves its partials right after its
+    single counter; before a call with 64 counters reuses the workspace, the
+    bytes between the two counter sections are zeroed, as the header asks."""
+    ws = Y.decode_workspace(8, 4096, 32, 8, 128, 32)
+    small = _inputs(1, 4096, 4, 1, 128, "bf16", 77)
+    big = _inputs(8, 4096, 32, 8, 128, "bf16", 78)
+    for (q, k, v), S_, rezero in ((small, 32, None), (big, 32, (1, 64)), (small, 8, None), (big, 4, (1, 64))):
+        if rezero is not None:
+            ws[rezero[0]:rezero[1]].zero_()
+        B, Hq = q.shape[0], q.shape[1]
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        Y.yoco_cross_attn_decode(dev(q), dev(k), dev(v), out, lse, num_splits=S_, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.all(ws[:B * k.shape[1]].view(torch.int32) == 0)
+        o_ref, lse_ref = O.decode_attention(q, k, v)
+        _compare(host(out).astype(np.float64), host(lse).astype(np.float64), o_ref, lse_ref, "bf16")
+
+
+def test_binding_default_workspace_follows_the_counters():
+    """Without a workspace argument the binding keeps one per (device, stream) and
+    zeroes the counters a larger call adds; sizes grow and shrink on one stream."""
+    for i, (B, Hkv, S_) in enumerate([(1, 1, 16), (4, 2, 8), (2, 2, 32), (8, 8, 4), (1, 1, 64), (8, 8, 0)]):
+        q, k, v = _inputs(B, 2000, 4 * Hkv, Hkv, 128, "bf16", 120 + i)
+        o, lse = _decode(dev(q), dev(k), dev(v), S_)
+        o_ref, lse_ref = O.decode_attention(q, k, v)
+        _compare(o, lse, o_ref, lse_ref, "bf16")
+
+
 def test_concurrent_streams_with_their_own_workspaces():
     """Decodes enqueued on four streams at once, each with its own workspace:
     their fused merges count tickets independently, and every result equals the

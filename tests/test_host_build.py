@@ -1,0 +1,52 @@
+"""Host-only builds of the native code, run on the CPU (no GPU needed):
+
+- the C ABI layer (yoco_api.cpp) with test-only launchers, under
+  AddressSanitizer and UndefinedBehaviorSanitizer: valid calls reach the
+  launchers with the promised parameters, launcher failures become
+  YOCO_ERR_LAUNCH, rejected calls launch nothing, and the decode's 32-bit row
+  offsets hold at the largest accepted cache length (tests/host_build/abi_driver.cpp);
+- the division by invariant integers the streaming kernels use
+  (tests/host_build/fastdiv_check.cpp), against plain division.
+
+The host compiler is g++ (the C ABI layer includes only the HIP runtime's API
+header), so no device code is built here."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "cross_layer_shared_amd", "csrc")
+HERE = os.path.join(ROOT, "tests", "host_build")
+ROCM_INCLUDE = "/opt/rocm/include"
+
+pytestmark = pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir(ROCM_INCLUDE),
+                                reason="needs g++ and the HIP runtime headers")
+
+COMMON = ["-std=c++20", "-g", "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INCLUDE, "-I", os.path.join(ROOT, "include"),
+          "-I", CSRC, "-I", HERE]
+
+
+def _build_and_run(tmp_path, name, sources, flags, env=None):
+    exe = str(tmp_path / name)
+    cmd = ["g++", *COMMON, *flags, *sources, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, f"build failed:\n{r.stderr[-4000:]}"
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", f"{run.stdout[-2000:]}\n{run.stderr[-4000:]}"
+
+
+def test_abi_layer_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    _build_and_run(tmp_path, "abi_driver",
+                   [os.path.join(CSRC, "yoco_api.cpp"), os.path.join(HERE, "launch_stubs.cpp"),
+                    os.path.join(HERE, "abi_driver.cpp")],
+                   ["-O1", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"],
+                   env)
+
+
+def test_fastdiv_equals_division(tmp_path):
+    # fastdiv.h is included by the kernels too; its host path needs only the HIP host macros
+    _build_and_run(tmp_path, "fastdiv_check", [os.path.join(HERE, "fastdiv_check.cpp")],
+                   ["-O2", "-include", "hip/hip_runtime.h"])
