@@ -9,6 +9,7 @@ namespace yoco {
 hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream) {
   if (p.append) return launch_decode_append(p, bf16, stream);
   if (p.compose_on_read) return launch_decode_compose_on_read(p, bf16, stream);
+  if (bf16) return launch_decode_mfma(p, stream);
   return launch_mode<kPlain>(p, bf16, stream);
 }
 

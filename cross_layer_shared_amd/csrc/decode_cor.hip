@@ -6,6 +6,7 @@
 namespace yoco {
 
 hipError_t launch_decode_compose_on_read(const DecodeParams& p, bool bf16, hipStream_t stream) {
+  if (bf16) return launch_decode_mfma(p, stream);   // the arithmetic of the composed-cache decode, row for row
   return launch_mode<kComposeOnRead>(p, bf16, stream);
 }
 

@@ -281,6 +281,68 @@ constexpr int kPlain = 0;          // decode over a composed cache
 constexpr int kComposeOnRead = 1;  // K', V' formed per row from two raw caches
 constexpr int kAppend = 2;         // self-decoder step: compose and append the new row
 
+// Merge the wavefronts' softmax states of one split (in LDS: sm_acc [NW][G][D],
+// sm_m, sm_l [NW][G], log2 domain) and write the split's result: the output
+// itself when there is one split, else the split's partial, and then, with
+// tickets, the fused merge by the last workgroup of (b, g) to finish. Called by
+// every thread of the workgroup after a barrier that follows the LDS writes.
+template <int D, int G, int NW>
+__device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int g, int split,
+                                             const float* __restrict__ sm_acc, const float* __restrict__ sm_m,
+                                             const float* __restrict__ sm_l) {
+  // ---- merge the wavefronts and write this split's result ----
+  const int h0 = g * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
+    const int hh = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * G + hh]);
+    float Lsum = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      float m = sm_m[w * G + hh];
+      float wt = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+      Lsum += wt * sm_l[w * G + hh];
+      O += wt * sm_acc[(w * G + hh) * D + d];
+    }
+    const bool empty = !(Lsum > 0.f);
+    const float o = empty ? 0.f : O / Lsum;
+    const float lse = empty ? -INFINITY : (M + __log2f(Lsum)) * 0.69314718055994530942f;
+    const int h = h0 + hh;
+    if (p.num_splits == 1) {
+      p.out[((size_t)b * p.Hq + h) * D + d] = o;
+      if (p.lse && d == 0) p.lse[(size_t)b * p.Hq + h] = lse;
+    } else {
+      const size_t row = ((size_t)b * p.Hq + h) * p.num_splits + split;
+      if (p.tickets) {          // published to the merging workgroup, possibly on another XCD
+        store_agent(&p.part_o[row * D + d], o);
+        if (d == 0) store_agent(&p.part_lse[row], lse);
+      } else {
+        p.part_o[row * D + d] = o;
+        if (d == 0) p.part_lse[row] = lse;
+      }
+    }
+  }
+  if (p.num_splits == 1 || p.tickets == nullptr) return;
+
+  // ---- fused merge: the last workgroup of (b, g) to finish merges all splits ----
+  // Every wave drains its partial stores (acknowledged at agent scope) before
+  // the barrier, so the ticket is taken only after the whole partial is visible.
+  __shared__ int sm_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(&p.tickets[b * p.Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = old == (unsigned)(p.num_splits - 1);
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  merge_splits<D, G, NW, true>(p.part_o, p.part_lse, p.num_splits, b * p.Hq + h0, p.out, p.lse);
+  if (threadIdx.x == 0)   // ready for the next call
+    __hip_atomic_store(&p.tickets[b * p.Hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <bool BF16, int D, int G, int NW, bool PREFETCH, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   constexpr bool COR = MODE == kComposeOnRead;
@@ -587,57 +649,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- merge the wavefronts and write this split's result ----
-  const int h0 = g * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
-    const int hh = idx / D, d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
-    float Lsum = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      float m = sm_m[w][hh];
-      float wt = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-      Lsum += wt * sm_l[w][hh];
-      O += wt * sm_acc[w][hh][d];
-    }
-    const bool empty = !(Lsum > 0.f);
-    const float o = empty ? 0.f : O / Lsum;
-    const float lse = empty ? -INFINITY : (M + __log2f(Lsum)) * 0.69314718055994530942f;
-    const int h = h0 + hh;
-    if (p.num_splits == 1) {
-      p.out[((size_t)b * p.Hq + h) * D + d] = o;
-      if (p.lse && d == 0) p.lse[(size_t)b * p.Hq + h] = lse;
-    } else {
-      const size_t row = ((size_t)b * p.Hq + h) * p.num_splits + split;
-      if (p.tickets) {          // published to the merging workgroup, possibly on another XCD
-        store_agent(&p.part_o[row * D + d], o);
-        if (d == 0) store_agent(&p.part_lse[row], lse);
-      } else {
-        p.part_o[row * D + d] = o;
-        if (d == 0) p.part_lse[row] = lse;
-      }
-    }
-  }
-  if (p.num_splits == 1 || p.tickets == nullptr) return;
-
-  // ---- fused merge: the last workgroup of (b, g) to finish merges all splits ----
-  // Every wave drains its partial stores (acknowledged at agent scope) before
-  // the barrier, so the ticket is taken only after the whole partial is visible.
-  __shared__ int sm_last;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add(&p.tickets[b * p.Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = old == (unsigned)(p.num_splits - 1);
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  merge_splits<D, G, NW, true>(p.part_o, p.part_lse, p.num_splits, b * p.Hq + h0, p.out, p.lse);
-  if (threadIdx.x == 0)   // ready for the next call
-    __hip_atomic_store(&p.tickets[b * p.Hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  finish_split<D, G, NW>(p, b, g, split, &sm_acc[0][0][0], &sm_m[0][0], &sm_l[0][0]);
 }
 
 // Standalone merge: one workgroup of 4 wavefronts per (b, group of 4 heads), one head per wavefront.
@@ -695,5 +707,7 @@ hipError_t launch_mode(const DecodeParams& p, bool bf16, hipStream_t s) {
 // Each mode is instantiated in a translation unit of its own (parallel builds).
 hipError_t launch_decode_compose_on_read(const DecodeParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_decode_append(const DecodeParams& p, bool bf16, hipStream_t stream);
+// The split pass of a bf16 decode over a composed cache on the matrix cores (decode_mfma.hip).
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace yoco
