@@ -1,16 +1,17 @@
-// Decode attention: the plain split pass (over a composed cache), the
-// dispatch to the other modes and the standalone merge. The kernels are in
-// decode_kernel.h.
+// Decode attention: the dispatch of the split pass (bf16 caches: the
+// matrix-core kernel of decode_mfma.hip; fp32 caches: the vector-ALU kernel of
+// decode_kernel.h, plain mode here, the other modes in their own translation
+// units) and the standalone merge.
 
 #include "decode_kernel.h"
 
 namespace yoco {
 
 hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream) {
-  if (p.append) return launch_decode_append(p, bf16, stream);
-  if (p.compose_on_read) return launch_decode_compose_on_read(p, bf16, stream);
-  if (bf16) return launch_decode_mfma(p, stream);
-  return launch_mode<kPlain>(p, bf16, stream);
+  if (bf16) return launch_decode_mfma(p, stream);   // every mode of a bf16 cache runs on the matrix cores
+  if (p.append) return launch_decode_append(p, stream);
+  if (p.compose_on_read) return launch_decode_compose_on_read(p, stream);
+  return launch_mode<kPlain>(p, stream);
 }
 
 hipError_t launch_decode_merge(const float* part_o, const float* part_lse, int B, int Hq, int D, int S, float* out,

@@ -696,17 +696,18 @@ hipError_t launch_nw(const DecodeParams& p, hipStream_t s) {
 }
 
 // The split pass in one mode, for every supported dtype, D, G and launch shape.
+// The vector-ALU split pass serves fp32 caches (bf16 caches take the
+// matrix-core kernel of decode_mfma.hip in every mode).
 template <int MODE>
-hipError_t launch_mode(const DecodeParams& p, bool bf16, hipStream_t s) {
-  if (bf16) return p.D == 64 ? launch_nw<true, 64, MODE>(p, s) : launch_nw<true, 128, MODE>(p, s);
+hipError_t launch_mode(const DecodeParams& p, hipStream_t s) {
   return p.D == 64 ? launch_nw<false, 64, MODE>(p, s) : launch_nw<false, 128, MODE>(p, s);
 }
 
 }  // namespace
 
-// Each mode is instantiated in a translation unit of its own (parallel builds).
-hipError_t launch_decode_compose_on_read(const DecodeParams& p, bool bf16, hipStream_t stream);
-hipError_t launch_decode_append(const DecodeParams& p, bool bf16, hipStream_t stream);
+// Each mode of the fp32 split pass is instantiated in a translation unit of its own (parallel builds).
+hipError_t launch_decode_compose_on_read(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_append(const DecodeParams& p, hipStream_t stream);
 // The split pass of a bf16 decode over a composed cache on the matrix cores (decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 

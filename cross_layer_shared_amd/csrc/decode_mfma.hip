@@ -74,6 +74,7 @@ __device__ __forceinline__ float rows_sum(float x) {
 template <int D, int G, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   constexpr bool COR = MODE == kComposeOnRead;   // K', V' formed per row from two raw caches
+  constexpr bool APP = MODE == kAppend;          // self-decoder step: compose and append the new row
   constexpr int NQK = D / 32;          // k-steps of the score product
   constexpr int NDB = D / 16;          // 16-dim blocks of O^T
   constexpr int VPAD = D + 32;         // LDS row stride of a V block (bf16); conflict-free transposing reads
@@ -98,7 +99,27 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
     len = len < 1 ? 1 : (len > p.T ? p.T : len);
   }
   const int ts = split * p.rows_per_split;
-  const int te = min(ts + p.rows_per_split, len);
+  // In append mode the cache supplies rows [0, len - 1); row len - 1 is the
+  // new token, composed and folded in by the split whose range holds it.
+  const int te = min(ts + p.rows_per_split, APP ? len - 1 : len);
+  const bool own_new = APP && split == (len - 1) / p.rows_per_split;
+
+  // Append mode: the owner's first wavefront loads the new token's K_1, K_i,
+  // V_1, V_i rows now (lanes 0 .. D/8 - 1, 8 elements each) and composes them
+  // after its stream.
+  __shared__ __attribute__((aligned(16))) __bf16 s_new[2][D];   // the composed new row: K', V'
+  u32x4_t nsrc[4] = {};
+  const bool new_lane = own_new && threadIdx.x < D / 8;
+  if constexpr (APP) {
+    if (new_lane) {
+      const View4* views[4] = {&p.nk1, &p.nki, &p.nv1, &p.nvi};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nsrc[i] = *reinterpret_cast<const u32x4_t*>(static_cast<const __bf16*>(views[i]->ptr) + (int64_t)b * views[i]->sb +
+                                                    (int64_t)g * views[i]->sh + (int64_t)(len - 1) * views[i]->st +
+                                                    8 * threadIdx.x);
+    }
+  }
 
   // Q^T operand: lane (lg, lr) holds query head g G + lr (zero for lr >= G),
   // dims 32 j + 8 lg .. + 8 of k-step j.
@@ -281,6 +302,54 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
     }
   }
 
+  // ---- append mode: compose the new row, write it into the cache and fold it
+  // into the first wavefront's state ----
+  if constexpr (APP) {
+    if (own_new && wave == 0) {
+      if (new_lane) {
+        u32x4_t kn, vn;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kn[w] = compose_dword<true>(nsrc[0][w], nsrc[1][w], p.cK1, p.cK2, p.termsK);
+          vn[w] = compose_dword<true>(nsrc[2][w], nsrc[3][w], p.cV1, p.cV2, p.termsV);
+        }
+        *reinterpret_cast<u32x4_t*>(const_cast<__bf16*>(static_cast<const __bf16*>(p.k.ptr)) + (int64_t)b * p.k.sb +
+                                    (int64_t)g * p.k.sh + (int64_t)(len - 1) * p.k.st + 8 * threadIdx.x) = kn;
+        *reinterpret_cast<u32x4_t*>(const_cast<__bf16*>(static_cast<const __bf16*>(p.v.ptr)) + (int64_t)b * p.v.sb +
+                                    (int64_t)g * p.v.sh + (int64_t)(len - 1) * p.v.st + 8 * threadIdx.x) = vn;
+        *reinterpret_cast<u32x4_t*>(&s_new[0][8 * threadIdx.x]) = kn;
+        *reinterpret_cast<u32x4_t*>(&s_new[1][8 * threadIdx.x]) = vn;
+      }
+      __builtin_amdgcn_wave_barrier();
+      // score of the new row for query lr: this lane's dims 32 j + 8 lg .. + 8, summed over the four rows
+      float x = 0.f;
+#pragma unroll
+      for (int j = 0; j < NQK; ++j) {
+        const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(&s_new[0][32 * j + 8 * lg]);
+        const u32x4_t qw = __builtin_bit_cast(u32x4_t, qf[j]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // element through a scalar first: a bit-cast straight from a vector
+          // element compiles to the first element only (all four times)
+          const uint32_t qe = qw[w], ke = kw[w];
+          x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qe), __builtin_bit_cast(bf16x2_t, ke), x,
+                                              false);
+        }
+      }
+      x = rows_sum(x) * sl;
+      const float m2 = fmaxf(m_run, x);
+      const float wo = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
+      const float wn = fast_exp2(x - m2);
+      l_run = l_run * wo + (lg == 0 ? wn : 0.f);   // the new row's weight counted once per query
+#pragma unroll
+      for (int n = 0; n < NDB; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[n][i] = __builtin_fmaf(wn, (float)s_new[1][16 * n + 4 * lg + i], o[n][i] * wo);
+      m_run = m2;
+    }
+  }
+
   // ---- this wavefront's state into LDS: lane (lg, q) holds dims 16 n + 4 lg + i of query q ----
   const float l_q = rows_sum(l_run);
   __syncthreads();   // every wavefront is done with its V buffer
@@ -325,6 +394,7 @@ hipError_t launch_mode_mfma(const DecodeParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
+  if (p.append) return launch_mode_mfma<kAppend>(p, stream);
   return p.compose_on_read ? launch_mode_mfma<kComposeOnRead>(p, stream) : launch_mode_mfma<kPlain>(p, stream);
 }
 
