@@ -15,8 +15,12 @@ one such layer, the causal chunked prefill over that workload's global cache
 (TFLOP/s over unmasked pairs), that prefill's cache path with and without the
 early exit, the compose-on-read comparator, one self-decoder decode step over
 16 layers (fused append against compose-then-decode), the two long-context
-decodes (131K tokens x 4 sequences; 1M tokens), cold-cache decode timings, and
-a plain device copy as the achievable-bandwidth reference.
+decodes (131K tokens x 4 sequences; 1M tokens), and the achievable-bandwidth
+probes (plain streaming kernels of libyoco_ceiling.so with the decode's and
+the compose's traffic patterns). Per-launch figures come from launches issued
+back to back in a HIP graph (replay time / launches); HBM-served ones rotate
+over enough distinct buffers that the 256 MB Infinity Cache holds none of a
+launch's inputs.
 
 cpu_baseline: the fp64 oracle (as it stands) timed on the host cores over a
 bounded sample of the headline workload (a few of its decode layers).
@@ -698,7 +702,8 @@ def main():
     cold_ms = h["decode_cold_ms"]
     traffic = None if traffic_bytes is None else traffic_bytes / (cold_ms * 1e-3) / 1e9
     ceil = extra.get("ceiling", {}).get("read_128MiB", {}).get("hbm")
-    roofline = {"kernel": "decode_split_kernel<bf16, D=128, G=4> (split pass with fused merge)", "bound": "hbm",
+    roofline = {"kernel": "decode_mfma_kernel<D=128, G=4, 8 waves> (bf16 split pass on the matrix cores, fused merge)",
+                "bound": "hbm",
                 "achieved": h["decode_cold_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": h["decode_cold_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                 "traffic_bytes_per_launch": traffic_bytes,
