@@ -82,6 +82,16 @@ __device__ __forceinline__ s16x4 read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<__bf16*>(p)));
 }
+// The same read through a restrict-qualified pointer. Once inlined, the read
+// carries alias-scope metadata, and the compiler then no longer makes it wait
+// for every direct global-to-LDS load in flight (it cannot tell which LDS
+// bytes those write, and a plain transposing read carries no alias
+// information). The kernel that uses it orders its direct loads and reads
+// with its own waits and barriers.
+__device__ __forceinline__ s16x4 read_tr16_scoped(const __bf16* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<__bf16*>(p)));
+}
 
 // Row of a 32-key block that MFMA row i carries: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm_key(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -473,14 +483,453 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined kernel (D = 128). A SIMD's matrix core and its vector
+// ALU overlap well only when one wavefront interleaves both kinds of
+// instruction: a wavefront issuing MFMAs back to back leaves the other
+// wavefront of its SIMD few VALU issue slots, whereas VALU instructions placed
+// between a wavefront's own independent MFMAs run in their shadow. So every
+// wavefront runs the whole pipeline itself, in 64-key steps. Step u, with the
+// scores S(u) and the probabilities P(u - 1) in registers, is 32 MFMA slots,
+// each an MFMA and the VALU work it shadows, fenced so the compiler keeps the
+// order:
+//   slots  0-15  PV of P(u - 1) (keys 0-31, then 32-63) | slots 0-7 scale and
+//                shift S(u), slots 8-15 exponentials of S(u) keys 0-31
+//   slots 16-31  scores S(u + 1) (keys 0-31, then 32-63) | slots 16-23
+//                exponentials of S(u) keys 32-63, slots 25-31 row maxima of
+//                S(u + 1) keys 0-31
+// then the maxima of keys 32-63 and the reference decision. Each register
+// block is overwritten right after its last reader, so S and P need one
+// buffer each.
+//
+// Lazy rescaling with the deferred PV product: the reference max may move at
+// the end of step u, once the maxima of S(u + 1) are known. The normaliser
+// then holds steps <= u and is rescaled at once; O holds steps <= u - 1 and
+// receives P(u), computed against the old reference, in step u + 1, so O's
+// factor is applied at the end of step u + 1.
+//
+// Data movement. K and V tiles reach LDS by direct loads (buffer_load ...
+// lds) three steps ahead, into three K slots and three V slots (unpadded
+// 256-byte rows; chunk c of row r at position c ^ (r % 16) in K, c ^ 4 (r % 4)
+// in V, so the 16-lane K operand reads and the 32-lane transposing V reads
+// each touch every bank once). The PV operand needs 8 consecutive keys of one
+// dim per lane; the transposing LDS read delivers 4 per 8-byte read at a
+// quarter of the rate of 16-byte reads, so instead of every wavefront
+// transposing every tile, the workgroup transposes each V tile once (each
+// wavefront 8 keys by 128 dims) into a V^T slot (rows of 64 keys, 144-byte
+// stride), from which the PV operands are single 16-byte reads. Step u issues
+// the loads of K and V step u + 3 into slots u % 3 (last read in step u - 1),
+// transposes V step u + 1 into V^T slot (u + 1) % 3 (last read by PV in step
+// u - 1), reads K slot (u + 1) % 3 and V^T slot (u - 1) % 3. Before the
+// barrier that ends step u each wavefront waits for all its loads but the four
+// just issued and for its LDS accesses. Rows past the cache prefix lie outside
+// the buffer range and load as zeros.
+template <int HPW, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_pipe_kernel(PrefillParams p) {
+  constexpr int D = 128;
+  constexpr int WQ = kWaves / HPW;
+  constexpr int kSK = 64;                  // keys per step
+  constexpr int kSB = kSK / 32;            // 32-key MFMA blocks per step
+  constexpr int kNQ = D / 16, kNDB = D / 32;
+  constexpr int kNS = 3;                   // LDS slots per tensor
+  constexpr int kRowB = D * 2;             // bytes per stored K or V row
+  constexpr int kSlotB = kSK * kRowB;      // 16 KiB
+  constexpr int kVBase = kNS * kSlotB;     // V slots follow the K slots
+  constexpr int kVTRow = kSK * 2 + 16;     // bytes per V^T row (64 keys + pad)
+  constexpr int kVTSlotB = D * kVTRow;     // 18 KiB
+  constexpr int kVTBase = 2 * kNS * kSlotB;
+  constexpr int kLoads = kSK / 4 / kWaves; // direct loads (4 rows each) per wavefront, tensor and step
+  constexpr int kBufWord3 = 0x00020000;    // raw buffer resource, 32-bit data format
+  __shared__ __attribute__((aligned(16))) char lds[kVTBase + kNS * kVTSlotB];   // 150 KiB
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 5;
+  const int j = lane & 31;
+  const int ngrp = p.Hq / HPW;
+  const int npair = ngrp * p.B;
+  const int n_qgroups = (int)gridDim.x / npair;
+  int pair, qlin;
+  {
+    const int L = blockIdx.x;
+    if (npair % 8 == 0) {   // workgroup L runs on XCD L % 8: keep each (b, head group) on one XCD
+      const int x = L % 8, i = L / 8, ppx = npair / 8;
+      pair = x + 8 * (i % ppx);
+      qlin = i / ppx;
+    } else {
+      pair = L % npair;
+      qlin = L / npair;
+    }
+  }
+  const int qg = n_qgroups - 1 - qlin;
+  const int hgrp = pair % ngrp;
+  const int h = hgrp * HPW + (wave % HPW);
+  const int g = (hgrp * HPW) / (p.Hq / p.Hkv);
+  const int b = pair / ngrp;
+  const int c_wg = qg * (WQ * kQB);
+  const int c_w = c_wg + (wave / HPW) * kQB;
+  const int c_hi = min(c_wg + WQ * kQB, p.C);
+  const int kv_len = p.p0 + c_hi;
+  const int n = (kv_len + kSK - 1) / kSK;                 // steps
+  const int fm = min((p.p0 + c_wg) / kSK, n);              // first step whose scores need the causal mask
+
+  // no slot ever holds a non-finite leftover: zero the LDS before the first load lands
+  for (int i = tid; i < (int)(sizeof(lds) / 16); i += kThreads) reinterpret_cast<u32x4*>(lds)[i] = u32x4{0u, 0u, 0u, 0u};
+
+  const int c_me = min(c_w + j, p.C - 1);
+  const int pos = p.p0 + c_w + j;
+  bf16x8 qf[kNQ];
+  {
+    const __bf16* qrow = static_cast<const __bf16*>(p.q) + (((size_t)b * p.C + c_me) * p.Hq + h) * D + 8 * q;
+#pragma unroll
+    for (int c = 0; c < kNQ; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c);
+  }
+  __syncthreads();   // the zero fill is done before any direct load is issued
+
+  // direct loads: load i of wavefront w writes rows 8w + 4i + lane/16 of a slot, 16 bytes at position lane % 16
+  const int64_t kst_b = p.k.st * 2, vst_b = p.v.st * 2;
+  const char* kb = static_cast<const char*>(p.k.ptr) + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh) * 2;
+  const char* vb = static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh) * 2;
+  uint32_t koff[kLoads], voff[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = 8 * wave + 4 * i + (lane >> 4), ps = lane & 15;
+    koff[i] = (uint32_t)(r * kst_b) + 16u * (uint32_t)(ps ^ (r & 15));
+    voff[i] = (uint32_t)(r * vst_b) + 16u * (uint32_t)(ps ^ (4 * (r & 3)));
+  }
+  auto issue = [&](const char* base, int64_t st_b, const uint32_t* off, int x, int slot_byte) {
+    const int rows = min(kv_len - kSK * x, kSK);
+    const uint32_t bytes = rows > 0 ? (uint32_t)((int64_t)(rows - 1) * st_b + kRowB) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + (int64_t)x * kSK * st_b), (short)0, (int)bytes, kBufWord3);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + slot_byte + (8 * wave + 4 * i) * kRowB), 16, off[i], 0, 0, 0);
+  };
+  auto issue_k = [&](int x, int slot) { issue(kb, kst_b, koff, x, slot * kSlotB); };
+  auto issue_v = [&](int x, int slot) { issue(vb, vst_b, voff, x, kVBase + slot * kSlotB); };
+
+  // LDS addresses (bytes). K operand of k-step c at aK[c] (+ slot, + 32-key block).
+  const int pk = perm_key(j);
+  const uint32_t aK0 = (uint32_t)(pk * kRowB + 16 * (q ^ (pk & 15)));
+  uint32_t aK[kNQ];
+#pragma unroll
+  for (int c = 0; c < kNQ; ++c) aK[c] = aK0 ^ (32u * c);
+  // Transposing reads of a V tile: wavefront w covers keys kb_w .. +4 and kb_w + 8 .. +4
+  // (kb_w = 16 (w / 2) + 4 (w % 2)) of all 128 dims, one read per 32-dim block; lane
+  // (gq, i) of a read receives dim 16 (gq % 2) + i of 4 consecutive keys.
+  const int gq = lane >> 4, sl16 = lane & 15, r4 = sl16 >> 2;
+  const int kb_w = 16 * (wave >> 1) + 4 * (wave & 1);
+  const uint32_t aT0 = (uint32_t)(kVBase + (kb_w + 8 * (gq >> 1) + r4) * kRowB + 64 * r4 + 32 * (gq & 1) +
+                                  16 * ((sl16 >> 1) & 1) + 8 * (sl16 & 1));
+  uint32_t aT[kNDB];
+#pragma unroll
+  for (int db = 0; db < kNDB; ++db) aT[db] = aT0 ^ (64u * db);
+  // where those 4 keys land in V^T, and where lane l reads its PV operand (dim l % 32, keys 8 (l / 32) .. +8)
+  const uint32_t aW = (uint32_t)(kVTBase + (16 * (gq & 1) + sl16) * kVTRow + 2 * (kb_w + 8 * (gq >> 1)));
+  const uint32_t aP = (uint32_t)(kVTBase + j * kVTRow + 16 * q);
+
+  f32x16 o_acc[kNDB];
+#pragma unroll
+  for (int db = 0; db < kNDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
+  float m_ref = -INFINITY;   // reference max (log2 domain) the exponentials subtract
+  float m_use = 0.f;         // m_ref, or 0 while it is -inf
+  float l_run = 0.f;         // this lane's share of the normaliser
+  float pend = 1.f;          // factor O still owes (deferred rescale)
+  bool have_pend = false;    // wave-uniform
+  float mt_next = -INFINITY; // scaled max of the next step's scores
+  const float sl = p.scale_log2;
+  f32x16 sc[kSB];            // scores of one step (raw, then scaled and shifted)
+  u32x4 pw[kSB][2];          // bf16 probabilities of one step, packed in pairs (P^T operands)
+  s16x4 tv[kNDB];            // this wavefront's share of a V tile, transposed
+
+  auto transpose_read1 = [&](int vslot_byte, int db) {
+    tv[db] = read_tr16_scoped(reinterpret_cast<const __bf16*>(lds + aT[db] + vslot_byte));
+  };
+  auto transpose_write1 = [&](int vtslot_byte, int db) {
+    *reinterpret_cast<s16x4*>(lds + aW + vtslot_byte + db * 32 * kVTRow) = tv[db];
+  };
+  auto transpose_read = [&](int vslot_byte) {
+#pragma unroll
+    for (int db = 0; db < kNDB; ++db) transpose_read1(vslot_byte, db);
+  };
+  auto transpose_write = [&](int vtslot_byte) {
+#pragma unroll
+    for (int db = 0; db < kNDB; ++db) transpose_write1(vtslot_byte, db);
+  };
+  auto pv_operand = [&](int vtslot_byte, int hb, int hs, int db) {
+    return *reinterpret_cast<const bf16x8*>(lds + aP + vtslot_byte + db * 32 * kVTRow + (32 * hb + 16 * hs) * 2);
+  };
+  auto k_operand = [&](int kslot_byte, int hb, int c) {
+    return *reinterpret_cast<const bf16x8*>(lds + aK[c] + kslot_byte + hb * 32 * kRowB);
+  };
+  auto qk_block = [&](int kslot_byte, int hb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[hb][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kNQ; ++c)
+      sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kslot_byte, hb, c), qf[c], sc[hb], 0, 0, 0);
+  };
+  auto pv_block = [&](int vtslot_byte, int hb) {
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int db = 0; db < kNDB; ++db)
+        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand(vtslot_byte, hb, hs, db),
+                                                            __builtin_bit_cast(bf16x8, pw[hb][hs]), o_acc[db], 0, 0, 0);
+  };
+  auto mask_block = [&](int u, int hb) {
+    const int lim = pos - u * kSK - 8 * q;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * hb + perm_key(8 * (r >> 2) + (r & 3)) > lim) sc[hb][r] = -INFINITY;
+  };
+  auto max_block = [&](int hb) {
+    float m = fmaxf(sc[hb][0], sc[hb][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) m = fmaxf(fmaxf(m, sc[hb][r]), sc[hb][r + 1]);
+    return m;
+  };
+  auto scale_block = [&](int hb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_use);
+  };
+  // exponentials of two scaled scores, rounded to a bf16 pair in pw; the
+  // normaliser sums exactly the rounded values (dot2 against (1, 1))
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto exp_pair = [&](int hb, int hs, int e, float acc) {
+    const uint32_t w = pack2(fast_exp2(sc[hb][8 * hs + 2 * e]), fast_exp2(sc[hb][8 * hs + 2 * e + 1]));
+    pw[hb][hs][e] = w;
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+  };
+  auto exp_block = [&](int hb) {
+    float a = 0.f, c = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a = exp_pair(hb, 0, e, a);
+      c = exp_pair(hb, 1, e, c);
+    }
+    return a + c;
+  };
+  // end of step: O's deferred factor, then the reference for the next step
+  auto step_end = [&](bool decide) {
+    if (have_pend) {
+#pragma unroll
+      for (int db = 0; db < kNDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o_acc[db][r] *= pend;
+      have_pend = false;
+    }
+    if (decide && __builtin_amdgcn_ballot_w64(mt_next > m_ref + kLazy)) {
+      const float m_new = fmaxf(m_ref, mt_next);
+      pend = fast_exp2(m_ref - ((m_new == -INFINITY) ? 0.f : m_new));
+      l_run *= pend;
+      have_pend = true;
+      m_ref = m_new;
+    }
+    m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  };
+  // every load but the four just issued has landed in LDS, every LDS access is done, then the barrier
+  auto step_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kLoads));   // vmcnt(2 kLoads) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // P(u) and the normaliser are read only in later steps; without this the
+  // compiler sinks the exponentials out of the step, past its MFMAs, to just
+  // before the barrier
+  auto anchor = [&] {
+#pragma unroll
+    for (int hb = 0; hb < kSB; ++hb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) asm volatile("" : "+v"(pw[hb][hs]));
+    asm volatile("" : "+v"(l_run));
+  };
+
+  // steady step u (1 <= u, u + 1 < fm; T = u % 3): the 32 fenced slots
+  auto step_fast = [&]<int T>(int u) {
+    constexpr int KS = ((T + 1) % kNS) * kSlotB;          // K step u + 1
+    constexpr int VTR = ((T + 2) % kNS) * kVTSlotB;       // V^T step u - 1
+    constexpr int VSRC = ((T + 1) % kNS) * kSlotB;        // V step u + 1, to transpose
+    constexpr int VTW = ((T + 1) % kNS) * kVTSlotB;
+    constexpr int kPV = 2 * kSB * kNDB, kQK = kSB * kNQ;   // 16 + 16 slots
+    issue_k(u + 3, T);
+    issue_v(u + 3, T);
+    bf16x8 opnd[kPV + kQK];
+    auto fetch = [&](int t) {
+      if (t < kPV)
+        opnd[t] = pv_operand(VTR, t / (2 * kNDB), (t / kNDB) % 2, t % kNDB);
+      else
+        opnd[t] = k_operand(KS, (t - kPV) / kNQ, (t - kPV) % kNQ);
+    };
+    fetch(0);
+    fetch(1);
+    fetch(2);
+    float la = 0.f, lc = 0.f, mb0 = 0.f;
+    const f32x16 zero = {};
+#pragma unroll
+    for (int t = 0; t < kPV + kQK; ++t) {
+      if (t + 3 < kPV) fetch(t + 3);
+      if (t + 4 >= kPV && t + 4 < kPV + kQK) fetch(t + 4);
+      // the V tile transposition rides on the score slots, whose operand reads are light
+      if (t >= 17 && t <= 23 && t % 2 == 1) transpose_read1(VSRC, (t - 17) / 2);
+      if (t >= 27 && t <= 30) transpose_write1(VTW, t - 27);
+      if (t < kPV) {
+        const int hb = t / (2 * kNDB), hs = (t / kNDB) % 2, db = t % kNDB;
+        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[t], __builtin_bit_cast(bf16x8, pw[hb][hs]), o_acc[db],
+                                                            0, 0, 0);
+      } else {
+        const int hb = (t - kPV) / kNQ, c = (t - kPV) % kNQ;
+        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[t], qf[c], c == 0 ? zero : sc[hb], 0, 0, 0);
+      }
+      if (t < 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[t / 4][4 * (t % 4) + i] = __builtin_fmaf(sc[t / 4][4 * (t % 4) + i], sl, -m_use);
+      } else if (t < 16) {
+        const int i = t - 8;
+        if (i % 2 == 0)
+          la = exp_pair(0, i / 4, i % 4, la);
+        else
+          lc = exp_pair(0, i / 4, i % 4, lc);
+      } else if (t < 24) {
+        const int i = t - 16;
+        if (i % 2 == 0)
+          la = exp_pair(1, i / 4, i % 4, la);
+        else
+          lc = exp_pair(1, i / 4, i % 4, lc);
+      } else if (t == 25) {
+        mb0 = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
+      } else if (t > 25) {
+        const int r = 3 + 3 * (t - 26);   // slots 26-30: elements 3-15
+#pragma unroll
+        for (int k2 = 0; k2 < 3; ++k2)
+          if (r + k2 < 16) mb0 = fmaxf(mb0, sc[0][r + k2]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += la + lc;
+    anchor();
+    const float mb1 = max_block(1);
+    mt_next = xor32_max(fmaxf(mb0, mb1)) * sl;
+    step_end(true);
+    step_barrier();
+  };
+  // any step, with the products and the mask as it needs them
+  auto step_edge = [&](int u) {
+    const int T = u % kNS;
+    const int KS = ((T + 1) % kNS) * kSlotB, VTR = ((T + 2) % kNS) * kVTSlotB;
+    transpose_read(((T + 1) % kNS) * kSlotB);
+    issue_k(u + 3, T);
+    issue_v(u + 3, T);
+    scale_block(0);
+    scale_block(1);
+    if (u >= 1) {
+      pv_block(VTR, 0);
+      pv_block(VTR, 1);
+    }
+    l_run += exp_block(0) + exp_block(1);
+    anchor();
+    transpose_write(((T + 1) % kNS) * kVTSlotB);
+    const bool has_next = u + 1 < n;
+    if (has_next) {
+      qk_block(KS, 0);
+      qk_block(KS, 1);
+      if (u + 1 >= fm) {
+        mask_block(u + 1, 0);
+        mask_block(u + 1, 1);
+      }
+      mt_next = xor32_max(fmaxf(max_block(0), max_block(1))) * sl;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    step_end(has_next);
+    step_barrier();
+  };
+
+  // prologue: K and V steps 0-2 in flight; V step 0 transposed, the scores of step 0
+  issue_k(0, 0);
+  issue_v(0, 0);
+  issue_k(1, 1);
+  issue_v(1, 1);
+  issue_k(2, 2);
+  issue_v(2, 2);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (8 * kLoads));   // vmcnt: K and V step 0 (and the queries) landed
+  asm volatile("s_barrier" ::: "memory");
+  transpose_read(0);
+  qk_block(0, 0);
+  qk_block(0, 1);
+  transpose_write(0);
+  if (fm == 0) {
+    mask_block(0, 0);
+    mask_block(0, 1);
+  }
+  mt_next = xor32_max(fmaxf(max_block(0), max_block(1))) * sl;
+  step_end(true);
+  // K and V step 1 landed, V^T step 0 written; step 0 may overwrite K and V slot 0
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0070 | (4 * kLoads));
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  step_edge(0);
+  const int fast_end = fm - 1;   // steps 1 <= u < fast_end have u + 1 < fm <= n
+  int u = 1;
+  for (; u + 2 < fast_end; u += 3) {
+    step_fast.template operator()<1>(u);
+    step_fast.template operator()<2>(u + 1);
+    step_fast.template operator()<0>(u + 2);
+  }
+  for (; u < n; ++u) step_edge(u);
+  // PV of the last step (V^T written before the last barrier), then O's last deferred factor
+  pv_block(((n - 1) % kNS) * kVTSlotB, 0);
+  pv_block(((n - 1) % kNS) * kVTSlotB, 1);
+  step_end(false);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no direct load may land after the workgroup ends
+
+  const float l_tot = xor32_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  const int c_out = c_w + j;
+  if (c_out < p.C) {
+    const size_t row = (((size_t)b * p.C + c_out) * p.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < kNDB; ++db) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int d = 32 * db + 8 * rb + 4 * q;
+        const float o0 = o_acc[db][4 * rb] * inv, o1 = o_acc[db][4 * rb + 1] * inv;
+        const float o2 = o_acc[db][4 * rb + 2] * inv, o3 = o_acc[db][4 * rb + 3] * inv;
+        if constexpr (OUT_BF16) {
+          u32x2 w = {pack2(o0, o1), pack2(o2, o3)};
+          *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.out) + row + d) = w;
+        } else {
+          float4 w = make_float4(o0, o1, o2, o3);
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row + d) = w;
+        }
+      }
+    }
+    if (p.lse && q == 0) p.lse[((size_t)b * p.Hq + h) * p.C + c_out] = (m_ref + __log2f(l_tot)) * 0.69314718055994530942f;
+  }
+}
+
 template <int D, int HPW>
 hipError_t launch_hpw(const PrefillParams& p, hipStream_t s) {
   constexpr int WQ = kWaves / HPW;
   dim3 grid(((p.C + WQ * kQB - 1) / (WQ * kQB)) * (p.Hq / HPW) * p.B);
-  if (p.out_bf16)
-    prefill_kernel<D, HPW, true><<<grid, kThreads, 0, s>>>(p);
-  else
-    prefill_kernel<D, HPW, false><<<grid, kThreads, 0, s>>>(p);
+  if constexpr (D == 128) {
+    if (p.out_bf16)
+      prefill_pipe_kernel<HPW, true><<<grid, kThreads, 0, s>>>(p);
+    else
+      prefill_pipe_kernel<HPW, false><<<grid, kThreads, 0, s>>>(p);
+  } else {
+    if (p.out_bf16)
+      prefill_kernel<D, HPW, true><<<grid, kThreads, 0, s>>>(p);
+    else
+      prefill_kernel<D, HPW, false><<<grid, kThreads, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

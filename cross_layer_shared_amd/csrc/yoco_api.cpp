@@ -642,6 +642,9 @@ yoco_status yoco_cross_attn_prefill(const void* q, yoco_tensor4 k_cache, yoco_te
   if ((st = check_tensor("v_cache", v_cache, need, 2)) != YOCO_OK) return st;
   if ((st = check_row_stride("k_cache", k_cache, D)) != YOCO_OK) return st;
   if ((st = check_row_stride("v_cache", v_cache, D)) != YOCO_OK) return st;
+  // the kernel addresses the rows of a 64-key step with 32-bit byte offsets
+  if (k_cache.stride_t >= (int64_t(1) << 24) || v_cache.stride_t >= (int64_t(1) << 24))
+    return fail(YOCO_ERR_UNSUPPORTED, "prefill: cache stride_t must be below 2^24 elements");
   if (need > INT32_MAX / 2) return fail(YOCO_ERR_UNSUPPORTED, "cache too long");
   if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)D);
   if (!isfinite(scale)) return fail(YOCO_ERR_INVALID_ARG, "scale must be finite");
