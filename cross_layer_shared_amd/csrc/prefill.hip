@@ -641,7 +641,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float l_run = 0.f;         // this lane's share of the normaliser
   float pend = 1.f;          // factor O still owes (deferred rescale)
   bool have_pend = false;    // wave-uniform
-  float mt_next = -INFINITY; // scaled max of the next step's scores
   const float sl = p.scale_log2;
   f32x16 sc[kSB];            // scores of one step (raw, then scaled and shifted)
   u32x4 pw[kSB][2];          // bf16 probabilities of one step, packed in pairs (P^T operands)
@@ -715,8 +714,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     return a + c;
   };
-  // end of step: O's deferred factor, then the reference for the next step
-  auto step_end = [&](bool decide) {
+  // The reference decision for S(u), at the start of step u: mb0 (the
+  // maximum of S(u) keys 0-31) was taken in step u - 1, mb1 is taken here.
+  // Branch-free: without a move alpha is exactly 1.
+  float mb0_c = -INFINITY;
+  auto decide = [&](float mb1) {
+    const float mt = xor32_max(fmaxf(mb0_c, mb1)) * sl;
+    const bool need = __builtin_amdgcn_ballot_w64(mt > m_ref + kLazy) != 0;
+    const float m_new = need ? fmaxf(m_ref, mt) : m_ref;
+    const float alpha = fast_exp2(m_ref - ((m_new == -INFINITY) ? 0.f : m_new));
+    l_run *= alpha;
+    pend = alpha;
+    have_pend = need;
+    m_ref = m_new;
+    m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  };
+  // end of step u: O, now holding PV up to step u - 1 against the old
+  // reference, takes the factor decided at the start of the step
+  auto step_end = [&] {
     if (have_pend) {
 #pragma unroll
       for (int db = 0; db < kNDB; ++db)
@@ -724,14 +739,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int r = 0; r < 16; ++r) o_acc[db][r] *= pend;
       have_pend = false;
     }
-    if (decide && __builtin_amdgcn_ballot_w64(mt_next > m_ref + kLazy)) {
-      const float m_new = fmaxf(m_ref, mt_next);
-      pend = fast_exp2(m_ref - ((m_new == -INFINITY) ? 0.f : m_new));
-      l_run *= pend;
-      have_pend = true;
-      m_ref = m_new;
-    }
-    m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
   };
   // every load but the four just issued has landed in LDS, every LDS access is done, then the barrier
   auto step_barrier = [] {
@@ -750,16 +757,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int hs = 0; hs < 2; ++hs) asm volatile("" : "+v"(pw[hb][hs]));
     asm volatile("" : "+v"(l_run));
   };
+  // The first PV operands of the next step come from a V^T slot written two
+  // steps before; they are read before the barrier that ends a step, so the
+  // next step's first MFMA does not wait for LDS.
+  constexpr int kCarry = 3;
+  bf16x8 carry[kCarry];
+  auto prefetch_next = [&](int vtslot_byte) {
+#pragma unroll
+    for (int t = 0; t < kCarry; ++t) carry[t] = pv_operand(vtslot_byte, 0, t / kNDB, t % kNDB);
+  };
 
-  // steady step u (1 <= u, u + 1 < fm; T = u % 3): the 32 fenced slots
+  // Steady step u (1 <= u, u + 1 < fm; T = u % 3): 32 fenced slots.
+  //   slots  0-15  PV of P(u - 1) | 0: maxima of S(u) keys 32-63; 1: the
+  //                reference decision; 2-7 and 8-15 (one per slot): scale
+  //                and shift S(u); 8-15: exponentials of keys 0-31
+  //   slots 16-31  scores S(u + 1) | 16-23: exponentials of keys 32-63;
+  //                25-31: maxima of S(u + 1) keys 0-31
+  // The loads of step u + 3 go out in slot 3, the V tile transposition rides
+  // on the score slots, whose operand reads are light.
   auto step_fast = [&]<int T>(int u) {
     constexpr int KS = ((T + 1) % kNS) * kSlotB;          // K step u + 1
     constexpr int VTR = ((T + 2) % kNS) * kVTSlotB;       // V^T step u - 1
     constexpr int VSRC = ((T + 1) % kNS) * kSlotB;        // V step u + 1, to transpose
     constexpr int VTW = ((T + 1) % kNS) * kVTSlotB;
+    constexpr int VTN = T * kVTSlotB;                     // V^T step u, read by the next step
     constexpr int kPV = 2 * kSB * kNDB, kQK = kSB * kNQ;   // 16 + 16 slots
-    issue_k(u + 3, T);
-    issue_v(u + 3, T);
     bf16x8 opnd[kPV + kQK];
     auto fetch = [&](int t) {
       if (t < kPV)
@@ -767,16 +789,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       else
         opnd[t] = k_operand(KS, (t - kPV) / kNQ, (t - kPV) % kNQ);
     };
-    fetch(0);
-    fetch(1);
-    fetch(2);
+#pragma unroll
+    for (int t = 0; t < kCarry; ++t) opnd[t] = carry[t];
     float la = 0.f, lc = 0.f, mb0 = 0.f;
     const f32x16 zero = {};
 #pragma unroll
     for (int t = 0; t < kPV + kQK; ++t) {
-      if (t + 3 < kPV) fetch(t + 3);
+      if (t + kCarry < kPV) fetch(t + kCarry);
       if (t + 4 >= kPV && t + 4 < kPV + kQK) fetch(t + 4);
-      // the V tile transposition rides on the score slots, whose operand reads are light
+      if (t == 3) {
+        issue_k(u + 3, T);
+        issue_v(u + 3, T);
+      }
       if (t >= 17 && t <= 23 && t % 2 == 1) transpose_read1(VSRC, (t - 17) / 2);
       if (t >= 27 && t <= 30) transpose_write1(VTW, t - 27);
       if (t < kPV) {
@@ -787,11 +811,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int hb = (t - kPV) / kNQ, c = (t - kPV) % kNQ;
         sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[t], qf[c], c == 0 ? zero : sc[hb], 0, 0, 0);
       }
-      if (t < 8) {
+      if (t == 0) {
+        mb0 = max_block(1);   // held in mb0 until the decision
+      } else if (t == 1) {
+        decide(mb0);
+      } else if (t < 8) {
+        // 24 of the 32 scalings: block 0, then block 1 elements 0-7
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[t / 4][4 * (t % 4) + i] = __builtin_fmaf(sc[t / 4][4 * (t % 4) + i], sl, -m_use);
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * (t - 2) + i, hb = e / 16, r = e % 16;
+          sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_use);
+        }
       } else if (t < 16) {
         const int i = t - 8;
+        sc[1][8 + i] = __builtin_fmaf(sc[1][8 + i], sl, -m_use);
         if (i % 2 == 0)
           la = exp_pair(0, i / 4, i % 4, la);
         else
@@ -812,17 +845,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    mb0_c = mb0;
     l_run += la + lc;
     anchor();
-    const float mb1 = max_block(1);
-    mt_next = xor32_max(fmaxf(mb0, mb1)) * sl;
-    step_end(true);
+    asm volatile("" : "+v"(mb0_c));
+    prefetch_next(VTN);
+    step_end();
     step_barrier();
   };
   // any step, with the products and the mask as it needs them
   auto step_edge = [&](int u) {
     const int T = u % kNS;
     const int KS = ((T + 1) % kNS) * kSlotB, VTR = ((T + 2) % kNS) * kVTSlotB;
+    decide(max_block(1));
     transpose_read(((T + 1) % kNS) * kSlotB);
     issue_k(u + 3, T);
     issue_v(u + 3, T);
@@ -835,18 +870,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     l_run += exp_block(0) + exp_block(1);
     anchor();
     transpose_write(((T + 1) % kNS) * kVTSlotB);
-    const bool has_next = u + 1 < n;
-    if (has_next) {
+    if (u + 1 < n) {
       qk_block(KS, 0);
       qk_block(KS, 1);
       if (u + 1 >= fm) {
         mask_block(u + 1, 0);
         mask_block(u + 1, 1);
       }
-      mt_next = xor32_max(fmaxf(max_block(0), max_block(1))) * sl;
+      mb0_c = max_block(0);
     }
+    prefetch_next(T * kVTSlotB);
     __builtin_amdgcn_sched_barrier(0);
-    step_end(has_next);
+    step_end();
     step_barrier();
   };
 
@@ -867,8 +902,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     mask_block(0, 0);
     mask_block(0, 1);
   }
-  mt_next = xor32_max(fmaxf(max_block(0), max_block(1))) * sl;
-  step_end(true);
+  mb0_c = max_block(0);
   // K and V step 1 landed, V^T step 0 written; step 0 may overwrite K and V slot 0
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0070 | (4 * kLoads));
@@ -884,10 +918,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     step_fast.template operator()<0>(u + 2);
   }
   for (; u < n; ++u) step_edge(u);
-  // PV of the last step (V^T written before the last barrier), then O's last deferred factor
+  // PV of the last step (V^T written before the last barrier); O owes no factor: the last one was applied at the end of step n - 1
   pv_block(((n - 1) % kNS) * kVTSlotB, 0);
   pv_block(((n - 1) % kNS) * kVTSlotB, 1);
-  step_end(false);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no direct load may land after the workgroup ends
 
   const float l_tot = xor32_sum(l_run);
