@@ -740,10 +740,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       have_pend = false;
     }
   };
-  // every load but the four just issued has landed in LDS, every LDS access is done, then the barrier
+  // Every direct load but the four just issued has landed in LDS, then the
+  // barrier. LDS reads may still be in flight: all but the next step's first
+  // PV operands were consumed by this step's MFMAs, and those read a V^T slot
+  // that is not rewritten before step u + 2. This step's V^T writes complete
+  // before any later LDS read of this wavefront returns (LDS operations
+  // complete in order), so before the next barrier.
   auto step_barrier = [] {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kLoads));   // vmcnt(2 kLoads) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads));   // vmcnt(2 kLoads)
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
