@@ -17,8 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libyoco.so")
-SOURCES = ["yoco_api.cpp", "compose.hip", "compose_backward.hip", "decode.hip", "decode_cor.hip", "decode_append.hip",
-           "decode_mfma.hip", "decode_noalloc.hip", "prefill.hip"]
+SOURCES = ["yoco_api.cpp", "compose.hip", "compose_backward.hip", "decode.hip", "decode_mfma.hip", "decode_noalloc.hip",
+           "prefill.hip"]
 CEILING_LIB = os.path.join(PKG, "libyoco_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"

@@ -1,7 +1,6 @@
 // Decode attention: the dispatch of the split pass (bf16 caches: the
 // matrix-core kernel of decode_mfma.hip; fp32 caches: the vector-ALU kernel of
-// decode_kernel.h, plain mode here, the other modes in their own translation
-// units) and the standalone merge.
+// decode_kernel.h in its three modes) and the standalone merge.
 
 #include "decode_kernel.h"
 
@@ -9,8 +8,8 @@ namespace yoco {
 
 hipError_t launch_decode_partial(const DecodeParams& p, bool bf16, hipStream_t stream) {
   if (bf16) return launch_decode_mfma(p, stream);   // every mode of a bf16 cache runs on the matrix cores
-  if (p.append) return launch_decode_append(p, stream);
-  if (p.compose_on_read) return launch_decode_compose_on_read(p, stream);
+  if (p.append) return launch_mode<kAppend>(p, stream);
+  if (p.compose_on_read) return launch_mode<kComposeOnRead>(p, stream);
   return launch_mode<kPlain>(p, stream);
 }
 

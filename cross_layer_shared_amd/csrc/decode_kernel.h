@@ -705,9 +705,6 @@ hipError_t launch_mode(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Each mode of the fp32 split pass is instantiated in a translation unit of its own (parallel builds).
-hipError_t launch_decode_compose_on_read(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_append(const DecodeParams& p, hipStream_t stream);
 // The split pass of a bf16 decode over a composed cache on the matrix cores (decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 

@@ -217,6 +217,16 @@ def test_prefill_rejects(lib, kw, status):
     assert Y.yoco_last_error() != ""
 
 
+def test_prefill_rejects_row_strides_past_its_32_bit_step_offsets(lib):
+    """The prefill addresses the 64 rows of a step with 32-bit byte offsets
+    from a per-step base, so a cache row stride of 2^24 elements or more is
+    refused."""
+    big = t4(BASE + (1 << 28), rows=8192, sb=0, sh=0, st=1 << 24)
+    assert prefill(lib, B=1, Hq=4, Hkv=1, k=big) == UNSUPPORTED
+    assert "stride_t" in Y.yoco_last_error()
+    assert prefill(lib, B=1, Hq=4, Hkv=1, v=big) == UNSUPPORTED
+
+
 def test_split_heuristic_and_workspace():
     # launch shapes measured best on MI355X for the three decode workloads
     assert Y.yoco_decode_num_splits(8, 4096, 32, 8, 128) == 4
