@@ -4,23 +4,20 @@
 // [0, p]; YOCO++ summary, section 3: prefill is compute-bound).
 //
 // Dense contraction on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
-// A workgroup of 8 wavefronts serves 8 (head, 32-query block) slots that share
-// one kv head (4 heads x 2 consecutive query blocks); it streams the cache in
-// 128-key tiles staged through LDS (two K and two V slots), so that all eight
-// wavefronts read each tile from LDS instead of from memory. K and V are both
-// stored row-major; the V operand of the PV product is read with the gfx950
-// transposing LDS read (ds_read_b64_tr_b16), which hands each lane 4
-// consecutive keys of one dim.
+// In both kernels here a workgroup of 8 wavefronts serves 8 (head, 32-query
+// block) slots that share one kv head (4 heads x 2 consecutive query blocks)
+// and stages the cache through LDS, so that all eight wavefronts read each
+// tile from LDS instead of from memory. At D = 128 the software-pipelined
+// prefill_pipe_kernel runs (its own comment below gives the step structure and
+// the data movement); at D = 64 prefill_kernel, whose two wavefronts per SIMD
+// take turns between an MFMA phase and a softmax phase over 128-key tiles
+// (half a tile apart at D = 128, where it ran before; in step at D = 64, whose
+// softmax phase dominates). The V operand of the PV product needs 4 or 8
+// consecutive keys of one dim per lane: prefill_kernel reads it with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16, 4 keys per read);
+// prefill_pipe_kernel transposes each V tile once into LDS.
 //
-// At D = 128 the two wavefronts on each SIMD (waves w and w + 4) run half a
-// tile apart: while one issues the MFMAs of a tile (PV of the previous tile,
-// scores of this one) the other runs the softmax of its tile on the VALU and
-// the exponential unit, and the workgroup barrier between the halves swaps
-// the roles. Run in step instead, both wavefronts would wait on the matrix
-// core at the same time and then both on the VALU. At D = 64 the MFMA phase
-// is half as long and the softmax phase dominates; there they run in step.
-//
-// Per wavefront and tile:
+// Per wavefront and tile of prefill_kernel (prefill_pipe_kernel: 64-key steps):
 //   S^T = K Q^T   (4 x 32 keys by 32 queries; D = 128 in 8 MFMA k-steps)
 //   online softmax per query column, log2 domain, fp32
 //   O^T += V^T P^T (4 x 32 dims by 32 queries; 128 keys in 8 MFMA k-steps)
@@ -29,12 +26,12 @@
 // become the P^T operand of the PV product without leaving the lane: the key
 // rows of each 32-key block are fed to the MFMA in the order that swaps bits 2
 // and 3 of the key index, which makes the 8 P values a lane holds for one PV
-// k-step 8 consecutive keys: two transposing reads of 4 keys each.
+// k-step 8 consecutive keys.
 // Probabilities are rounded to bf16 for the PV product, and the normaliser
 // sums the same rounded values.
 //
 // Every workgroup of one (sequence, kv head) streams the same K and V tiles,
-// so the tiles are loaded through the L2 (temporal loads), and the 1-D grid is
+// so the tiles are loaded through the L2, and the 1-D grid is
 // mapped so that all workgroups of one (sequence, head group) run on the same
 // XCD (workgroups are dealt round-robin to the 8 XCDs, each with its own L2):
 // the workgroups resident on an XCD walk one kv head's tiles nearly in step
