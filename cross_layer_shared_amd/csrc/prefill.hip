@@ -521,6 +521,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // barrier that ends step u each wavefront waits for all its loads but the four
 // just issued and for its LDS accesses. Rows past the cache prefix lie outside
 // the buffer range and load as zeros.
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (vmcnt is split over bits 3:0 and 15:14) and leaves the other
+// counters unconstrained.
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 template <int HPW, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_pipe_kernel(PrefillParams p) {
   constexpr int D = 128;
@@ -745,7 +750,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // complete in order), so before the next barrier.
   auto step_barrier = [] {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads));   // vmcnt(2 kLoads)
+    __builtin_amdgcn_s_waitcnt(vm_wait(2 * kLoads));
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -894,7 +899,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   issue_v(1, 1);
   issue_k(2, 2);
   issue_v(2, 2);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (8 * kLoads));   // vmcnt: K and V step 0 (and the queries) landed
+  __builtin_amdgcn_s_waitcnt(vm_wait(4 * kLoads));   // K and V step 0 landed (steps 1 and 2 may fly)
   asm volatile("s_barrier" ::: "memory");
   transpose_read(0);
   qk_block(0, 0);
@@ -907,7 +912,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   mb0_c = max_block(0);
   // K and V step 1 landed, V^T step 0 written; step 0 may overwrite K and V slot 0
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0x0070 | (4 * kLoads));
+  __builtin_amdgcn_s_waitcnt(vm_wait(2 * kLoads) & ~0x0F00);   // K and V step 1 landed, and lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
