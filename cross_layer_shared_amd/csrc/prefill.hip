@@ -775,9 +775,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
 
   // Steady step u (1 <= u, u + 1 < fm; T = u % 3): 32 fenced slots.
-  //   slots  0-15  PV of P(u - 1) | 0: maxima of S(u) keys 32-63; 1: the
-  //                reference decision; 2-7 and 8-15 (one per slot): scale
-  //                and shift S(u); 8-15: exponentials of keys 0-31
+  //   slots  0-15  PV of P(u - 1) | 0-1: maxima of S(u) keys 32-63; 2: the
+  //                reference decision; 3-15: scale and shift S(u) (keys 0-31
+  //                first); 8-15: exponentials of keys 0-31
   //   slots 16-31  scores S(u + 1) | 16-23: exponentials of keys 32-63;
   //                25-31: maxima of S(u + 1) keys 0-31
   // The loads of step u + 3 go out in slot 3, the V tile transposition rides
@@ -819,19 +819,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[t], qf[c], c == 0 ? zero : sc[hb], 0, 0, 0);
       }
       if (t == 0) {
-        mb0 = max_block(1);   // held in mb0 until the decision
+        mb0 = fmaxf(fmaxf(sc[1][0], sc[1][1]), sc[1][2]);   // maxima of S(u) keys 32-63, in mb0 until the decision
+#pragma unroll
+        for (int r = 3; r < 9; r += 2) mb0 = fmaxf(fmaxf(mb0, sc[1][r]), sc[1][r + 1]);
       } else if (t == 1) {
+#pragma unroll
+        for (int r = 9; r < 15; r += 2) mb0 = fmaxf(fmaxf(mb0, sc[1][r]), sc[1][r + 1]);
+        mb0 = fmaxf(mb0, sc[1][15]);
+      } else if (t == 2) {
         decide(mb0);
       } else if (t < 8) {
-        // 24 of the 32 scalings: block 0, then block 1 elements 0-7
+        // 20 of the 32 scalings: block 0, then block 1 elements 0-3
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = 4 * (t - 2) + i, hb = e / 16, r = e % 16;
+          const int e = 4 * (t - 3) + i, hb = e / 16, r = e % 16;
           sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_use);
         }
       } else if (t < 16) {
         const int i = t - 8;
-        sc[1][8 + i] = __builtin_fmaf(sc[1][8 + i], sl, -m_use);
+        sc[1][4 + i] = __builtin_fmaf(sc[1][4 + i], sl, -m_use);
+        if (i < 4) sc[1][12 + i] = __builtin_fmaf(sc[1][12 + i], sl, -m_use);
         if (i % 2 == 0)
           la = exp_pair(0, i / 4, i % 4, la);
         else
