@@ -638,9 +638,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int db = 0; db < kNDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
+  // The normaliser rides on the matrix core: one more MFMA per PV k-step with
+  // an A operand whose row 0 is all ones (lanes 0 and 32 hold it) and whose
+  // other rows are zero, so row 0 of l_acc accumulates the sum over keys of the
+  // bf16 probabilities P^T (exact products, fp32 sums), held by lanes 0-31 in
+  // element 0; it is rescaled together with O.
+  f32x16 l_acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) l_acc[r] = 0.f;
+  bf16x8 ones_row;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones_row[e] = (j == 0) ? (__bf16)1.0f : (__bf16)0.0f;
   float m_ref = -INFINITY;   // reference max (log2 domain) the exponentials subtract
   float m_use = 0.f;         // m_ref, or 0 while it is -inf
-  float l_run = 0.f;         // this lane's share of the normaliser
   float pend = 1.f;          // factor O still owes (deferred rescale)
   bool have_pend = false;    // wave-uniform
   const float sl = p.scale_log2;
@@ -677,11 +687,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   auto pv_block = [&](int vtslot_byte, int hb) {
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
+    for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll
       for (int db = 0; db < kNDB; ++db)
         o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand(vtslot_byte, hb, hs, db),
                                                             __builtin_bit_cast(bf16x8, pw[hb][hs]), o_acc[db], 0, 0, 0);
+      l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_row, __builtin_bit_cast(bf16x8, pw[hb][hs]), l_acc, 0, 0, 0);
+    }
   };
   auto mask_block = [&](int u, int hb) {
     const int lim = pos - u * kSK - 8 * q;
@@ -699,22 +711,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_use);
   };
-  // exponentials of two scaled scores, rounded to a bf16 pair in pw; the
-  // normaliser sums exactly the rounded values (dot2 against (1, 1))
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto exp_pair = [&](int hb, int hs, int e, float acc) {
-    const uint32_t w = pack2(fast_exp2(sc[hb][8 * hs + 2 * e]), fast_exp2(sc[hb][8 * hs + 2 * e + 1]));
-    pw[hb][hs][e] = w;
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+  // exponentials of two scaled scores, rounded to a bf16 pair in pw (the
+  // normaliser sums exactly these rounded values, in l_acc)
+  auto exp_pair = [&](int hb, int hs, int e) {
+    pw[hb][hs][e] = pack2(fast_exp2(sc[hb][8 * hs + 2 * e]), fast_exp2(sc[hb][8 * hs + 2 * e + 1]));
   };
   auto exp_block = [&](int hb) {
-    float a = 0.f, c = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      a = exp_pair(hb, 0, e, a);
-      c = exp_pair(hb, 1, e, c);
+      exp_pair(hb, 0, e);
+      exp_pair(hb, 1, e);
     }
-    return a + c;
   };
   // The reference decision for S(u), at the start of step u: mb0 (the
   // maximum of S(u) keys 0-31) was taken in step u - 1, mb1 is taken here.
@@ -725,7 +732,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const bool need = __builtin_amdgcn_ballot_w64(mt > m_ref + kLazy) != 0;
     const float m_new = need ? fmaxf(m_ref, mt) : m_ref;
     const float alpha = fast_exp2(m_ref - ((m_new == -INFINITY) ? 0.f : m_new));
-    l_run *= alpha;
     pend = alpha;
     have_pend = need;
     m_ref = m_new;
@@ -739,6 +745,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int db = 0; db < kNDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[db][r] *= pend;
+      l_acc[0] *= pend;   // the other elements of l_acc stay 0
       have_pend = false;
     }
   };
@@ -762,7 +769,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int hb = 0; hb < kSB; ++hb)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) asm volatile("" : "+v"(pw[hb][hs]));
-    asm volatile("" : "+v"(l_run));
   };
   // The first PV operands of the next step come from a V^T slot written two
   // steps before; they are read before the barrier that ends a step, so the
@@ -788,36 +794,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int VSRC = ((T + 1) % kNS) * kSlotB;        // V step u + 1, to transpose
     constexpr int VTW = ((T + 1) % kNS) * kVTSlotB;
     constexpr int VTN = T * kVTSlotB;                     // V^T step u, read by the next step
-    constexpr int kPV = 2 * kSB * kNDB, kQK = kSB * kNQ;   // 16 + 16 slots
-    bf16x8 opnd[kPV + kQK];
-    auto fetch = [&](int t) {
-      if (t < kPV)
-        opnd[t] = pv_operand(VTR, t / (2 * kNDB), (t / kNDB) % 2, t % kNDB);
+    constexpr int kOps = 2 * kSB * kNDB + kSB * kNQ;      // 16 PV + 16 score operands from LDS
+    constexpr int kPVS = 2 * kSB * (kNDB + 1);            // 20 PV-phase slots (4 PV MFMAs + 1 sum per k-step)
+    constexpr int kSlots = kPVS + kSB * kNQ;              // + 16 score slots
+    bf16x8 opnd[kOps];
+    auto fetch = [&](int o) {
+      if (o < 2 * kSB * kNDB)
+        opnd[o] = pv_operand(VTR, o / (2 * kNDB), (o / kNDB) % 2, o % kNDB);
       else
-        opnd[t] = k_operand(KS, (t - kPV) / kNQ, (t - kPV) % kNQ);
+        opnd[o] = k_operand(KS, (o - 2 * kSB * kNDB) / kNQ, (o - 2 * kSB * kNDB) % kNQ);
     };
+    // operand used at slot t (for a sum slot: the next one); operands are read
+    // three PV operands or four score operands ahead
+    auto op_at = [](int t) { return t < kPVS ? 4 * (t / 5) + (t % 5 == 4 ? 4 : t % 5) : 16 + (t - kPVS); };
+    auto want = [&](int t) { const int o = op_at(t); return min(o < 16 ? o + kCarry : o + 4, kOps - 1); };
 #pragma unroll
-    for (int t = 0; t < kCarry; ++t) opnd[t] = carry[t];
-    float la = 0.f, lc = 0.f, mb0 = 0.f;
+    for (int o = 0; o < kCarry; ++o) opnd[o] = carry[o];
+    float mb0 = 0.f;
     const f32x16 zero = {};
 #pragma unroll
-    for (int t = 0; t < kPV + kQK; ++t) {
-      if (t + kCarry < kPV) fetch(t + kCarry);
-      if (t + 4 >= kPV && t + 4 < kPV + kQK) fetch(t + 4);
+    for (int t = 0; t < kSlots; ++t) {
+#pragma unroll
+      for (int o = (t == 0 ? kCarry : want(t - 1) + 1); o <= want(t); ++o) fetch(o);
       if (t == 3) {
         issue_k(u + 3, T);
         issue_v(u + 3, T);
       }
-      if (t >= 17 && t <= 23 && t % 2 == 1) transpose_read1(VSRC, (t - 17) / 2);
-      if (t >= 27 && t <= 30) transpose_write1(VTW, t - 27);
-      if (t < kPV) {
-        const int hb = t / (2 * kNDB), hs = (t / kNDB) % 2, db = t % kNDB;
-        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[t], __builtin_bit_cast(bf16x8, pw[hb][hs]), o_acc[db],
-                                                            0, 0, 0);
+      if (t >= kPVS && t < kPVS + 4) transpose_read1(VSRC, t - kPVS);
+      if (t >= kPVS + 10 && t < kPVS + 14) transpose_write1(VTW, t - kPVS - 10);
+      if (t < kPVS) {
+        const int gk = t / 5, hb = gk / 2, hs = gk % 2, db = t % 5;
+        if (db < kNDB)
+          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[4 * gk + db], __builtin_bit_cast(bf16x8, pw[hb][hs]),
+                                                              o_acc[db], 0, 0, 0);
+        else
+          l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_row, __builtin_bit_cast(bf16x8, pw[hb][hs]), l_acc, 0, 0,
+                                                          0);
       } else {
-        const int hb = (t - kPV) / kNQ, c = (t - kPV) % kNQ;
-        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[t], qf[c], c == 0 ? zero : sc[hb], 0, 0, 0);
+        const int hb = (t - kPVS) / kNQ, c = (t - kPVS) % kNQ;
+        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[16 + (t - kPVS)], qf[c], c == 0 ? zero : sc[hb], 0, 0, 0);
       }
+      // VALU in the MFMA's shadow
       if (t == 0) {
         mb0 = fmaxf(fmaxf(sc[1][0], sc[1][1]), sc[1][2]);   // maxima of S(u) keys 32-63, in mb0 until the decision
 #pragma unroll
@@ -828,31 +845,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         mb0 = fmaxf(mb0, sc[1][15]);
       } else if (t == 2) {
         decide(mb0);
-      } else if (t < 8) {
-        // 20 of the 32 scalings: block 0, then block 1 elements 0-3
+      } else if (t < 10) {
+        // scalings: block 0 in slots 3-6, block 1 elements 0-11 in slots 7-9
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * (t - 3) + i, hb = e / 16, r = e % 16;
           sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_use);
         }
-      } else if (t < 16) {
-        const int i = t - 8;
-        sc[1][4 + i] = __builtin_fmaf(sc[1][4 + i], sl, -m_use);
+      } else if (t < 18) {
+        // exponentials of keys 0-31 (P(u - 1) keys 0-31 was read by slot 9);
+        // block 1 elements 12-15 scaled in slots 10-13
+        const int i = t - 10;
         if (i < 4) sc[1][12 + i] = __builtin_fmaf(sc[1][12 + i], sl, -m_use);
-        if (i % 2 == 0)
-          la = exp_pair(0, i / 4, i % 4, la);
-        else
-          lc = exp_pair(0, i / 4, i % 4, lc);
-      } else if (t < 24) {
-        const int i = t - 16;
-        if (i % 2 == 0)
-          la = exp_pair(1, i / 4, i % 4, la);
-        else
-          lc = exp_pair(1, i / 4, i % 4, lc);
-      } else if (t == 25) {
+        exp_pair(0, i / 4, i % 4);
+      } else if (t >= kPVS && t < kPVS + 8) {
+        // exponentials of keys 32-63 (P(u - 1) keys 32-63 was read by slot 19)
+        const int i = t - kPVS;
+        exp_pair(1, i / 4, i % 4);
+      } else if (t == kPVS + 9) {
         mb0 = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
-      } else if (t > 25) {
-        const int r = 3 + 3 * (t - 26);   // slots 26-30: elements 3-15
+      } else if (t > kPVS + 9) {
+        const int r = 3 + 3 * (t - kPVS - 10);   // slots 30-34: elements 3-15
 #pragma unroll
         for (int k2 = 0; k2 < 3; ++k2)
           if (r + k2 < 16) mb0 = fmaxf(mb0, sc[0][r + k2]);
@@ -860,7 +873,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       __builtin_amdgcn_sched_barrier(0);
     }
     mb0_c = mb0;
-    l_run += la + lc;
     anchor();
     asm volatile("" : "+v"(mb0_c));
     prefetch_next(VTN);
@@ -881,7 +893,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       pv_block(VTR, 0);
       pv_block(VTR, 1);
     }
-    l_run += exp_block(0) + exp_block(1);
+    exp_block(0);
+    exp_block(1);
     anchor();
     transpose_write(((T + 1) % kNS) * kVTSlotB);
     if (u + 1 < n) {
@@ -937,7 +950,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   pv_block(((n - 1) % kNS) * kVTSlotB, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no direct load may land after the workgroup ends
 
-  const float l_tot = xor32_sum(l_run);
+  const float l_tot = xor32_sum(l_acc[0]);
   const float inv = 1.0f / l_tot;
   const int c_out = c_w + j;
   if (c_out < p.C) {
