@@ -487,23 +487,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // wavefront of its SIMD few VALU issue slots, whereas VALU instructions placed
 // between a wavefront's own independent MFMAs run in their shadow. So every
 // wavefront runs the whole pipeline itself, in 64-key steps. Step u, with the
-// scores S(u) and the probabilities P(u - 1) in registers, is 32 MFMA slots,
+// scores S(u) and the probabilities P(u - 1) in registers, is 36 MFMA slots,
 // each an MFMA and the VALU work it shadows, fenced so the compiler keeps the
 // order:
-//   slots  0-15  PV of P(u - 1) (keys 0-31, then 32-63) | slots 0-7 scale and
-//                shift S(u), slots 8-15 exponentials of S(u) keys 0-31
-//   slots 16-31  scores S(u + 1) (keys 0-31, then 32-63) | slots 16-23
-//                exponentials of S(u) keys 32-63, slots 25-31 row maxima of
+//   slots  0-19  PV of P(u - 1), per 16-key slice four O MFMAs and one that
+//                adds the slice's probabilities into the normaliser (a ones
+//                row times P) | slots 0-1 maxima of S(u) keys 32-63, slot 2
+//                the reference decision, slots 3-13 scale and shift S(u),
+//                slots 10-17 exponentials of S(u) keys 0-31
+//   slots 20-35  scores S(u + 1) (keys 0-31, then 32-63) | slots 20-27
+//                exponentials of S(u) keys 32-63, slots 29-35 row maxima of
 //                S(u + 1) keys 0-31
-// then the maxima of keys 32-63 and the reference decision. Each register
-// block is overwritten right after its last reader, so S and P need one
-// buffer each.
+// Each register block is overwritten right after its last reader, so S and P
+// need one buffer each. The normaliser on the matrix core costs one MFMA per
+// slice and saves the row sums' adds on the vector ALU, which is the busier
+// unit: with the MFMAs taken out, a step's remaining instructions still take
+// longer than its MFMAs.
 //
-// Lazy rescaling with the deferred PV product: the reference max may move at
-// the end of step u, once the maxima of S(u + 1) are known. The normaliser
-// then holds steps <= u and is rescaled at once; O holds steps <= u - 1 and
-// receives P(u), computed against the old reference, in step u + 1, so O's
-// factor is applied at the end of step u + 1.
+// Lazy rescaling with the deferred PV product: the reference max may move
+// early in step u, once the maxima of S(u) are known and before S(u) is
+// exponentiated. O and the normaliser receive P(u - 1), computed against the
+// old reference, during step u, so both take the factor at the end of step u.
 //
 // Data movement. K and V tiles reach LDS by direct loads (buffer_load ...
 // lds) three steps ahead, into three K slots and three V slots (unpadded
@@ -780,12 +784,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int t = 0; t < kCarry; ++t) carry[t] = pv_operand(vtslot_byte, 0, t / kNDB, t % kNDB);
   };
 
-  // Steady step u (1 <= u, u + 1 < fm; T = u % 3): 32 fenced slots.
-  //   slots  0-15  PV of P(u - 1) | 0-1: maxima of S(u) keys 32-63; 2: the
-  //                reference decision; 3-15: scale and shift S(u) (keys 0-31
-  //                first); 8-15: exponentials of keys 0-31
-  //   slots 16-31  scores S(u + 1) | 16-23: exponentials of keys 32-63;
-  //                25-31: maxima of S(u + 1) keys 0-31
+  // Steady step u (1 <= u, u + 1 < fm; T = u % 3): 36 fenced slots.
+  //   slots  0-19  PV of P(u - 1) and the normaliser | 0-1: maxima of S(u)
+  //                keys 32-63; 2: the reference decision; 3-13: scale and
+  //                shift S(u) (keys 0-31 first); 10-17: exponentials of keys
+  //                0-31
+  //   slots 20-35  scores S(u + 1) | 20-27: exponentials of keys 32-63;
+  //                29-35: maxima of S(u + 1) keys 0-31
   // The loads of step u + 3 go out in slot 3, the V tile transposition rides
   // on the score slots, whose operand reads are light.
   auto step_fast = [&]<int T>(int u) {
