@@ -68,6 +68,7 @@ struct Dim {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -490,17 +491,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // scores S(u) and the probabilities P(u - 1) in registers, is 36 MFMA slots,
 // each an MFMA and the VALU work it shadows, fenced so the compiler keeps the
 // order:
-//   slots  0-19  PV of P(u - 1), per 16-key slice four O MFMAs and one that
-//                adds the slice's probabilities into the normaliser (a ones
-//                row times P) | slots 0-1 maxima of S(u) keys 32-63, slot 2
+//   slots  0-19  PV of P(u - 1), per 16-key slice four O MFMAs and a half-size
+//                one that adds the slice's probabilities into the normaliser
+//                (ones rows times P) | slots 0-1 maxima of S(u) keys 32-63, slot 2
 //                the reference decision, slots 3-13 scale and shift S(u),
 //                slots 10-17 exponentials of S(u) keys 0-31
 //   slots 20-35  scores S(u + 1) (keys 0-31, then 32-63) | slots 20-27
 //                exponentials of S(u) keys 32-63, slots 29-35 row maxima of
 //                S(u + 1) keys 0-31
 // Each register block is overwritten right after its last reader, so S and P
-// need one buffer each. The normaliser on the matrix core costs one MFMA per
-// slice and saves the row sums' adds on the vector ALU, which is the busier
+// need one buffer each. The normaliser on the matrix core costs half an MFMA
+// per slice and saves the row sums' adds on the vector ALU, which is the busier
 // unit: with the MFMAs taken out, a step's remaining instructions still take
 // longer than its MFMAs.
 //
@@ -642,17 +643,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int db = 0; db < kNDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
-  // The normaliser rides on the matrix core: one more MFMA per PV k-step with
-  // an A operand whose row 0 is all ones (lanes 0 and 32 hold it) and whose
-  // other rows are zero, so row 0 of l_acc accumulates the sum over keys of the
-  // bf16 probabilities P^T (exact products, fp32 sums), held by lanes 0-31 in
-  // element 0; it is rescaled together with O.
-  f32x16 l_acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) l_acc[r] = 0.f;
+  // The normaliser rides on the matrix core: one 16x16x32 MFMA per PV k-step
+  // takes the P^T operand register as its B operand. Read that way, lane
+  // groups 0 and 2 (lanes 0-15, 32-47) hold the 16 keys of queries 0-15 in
+  // their k positions, groups 1 and 3 those of queries 16-31. The A operand
+  // has ones where row 0 meets groups 0 and 2 and where row 1 meets groups 1
+  // and 3, zeros elsewhere, so row 0 of l_acc accumulates the sum over keys of
+  // the bf16 probabilities of queries 0-15 and row 1 that of queries 16-31
+  // (exact products, fp32 sums), in elements 0 and 1 of lanes 0-15. This
+  // needs only that A and B spread k over lanes and elements alike. l_acc is
+  // rescaled together with O.
+  f32x4 l_acc = {0.f, 0.f, 0.f, 0.f};
   bf16x8 ones_row;
+  {
+    const int g = lane >> 4, r16 = lane & 15;
+    const bool one = (r16 == 0 && (g & 1) == 0) || (r16 == 1 && (g & 1) == 1);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ones_row[e] = (j == 0) ? (__bf16)1.0f : (__bf16)0.0f;
+    for (int e = 0; e < 8; ++e) ones_row[e] = one ? (__bf16)1.0f : (__bf16)0.0f;
+  }
   float m_ref = -INFINITY;   // reference max (log2 domain) the exponentials subtract
   float m_use = 0.f;         // m_ref, or 0 while it is -inf
   float pend = 1.f;          // factor O still owes (deferred rescale)
@@ -696,7 +704,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int db = 0; db < kNDB; ++db)
         o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pv_operand(vtslot_byte, hb, hs, db),
                                                             __builtin_bit_cast(bf16x8, pw[hb][hs]), o_acc[db], 0, 0, 0);
-      l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_row, __builtin_bit_cast(bf16x8, pw[hb][hs]), l_acc, 0, 0, 0);
+      l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, __builtin_bit_cast(bf16x8, pw[hb][hs]), l_acc, 0, 0, 0);
     }
   };
   auto mask_block = [&](int u, int hb) {
@@ -750,6 +758,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[db][r] *= pend;
       l_acc[0] *= pend;   // the other elements of l_acc stay 0
+      l_acc[1] *= pend;
       have_pend = false;
     }
   };
@@ -833,7 +842,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[4 * gk + db], __builtin_bit_cast(bf16x8, pw[hb][hs]),
                                                               o_acc[db], 0, 0, 0);
         else
-          l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_row, __builtin_bit_cast(bf16x8, pw[hb][hs]), l_acc, 0, 0,
+          l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, __builtin_bit_cast(bf16x8, pw[hb][hs]), l_acc, 0, 0,
                                                           0);
       } else {
         const int hb = (t - kPVS) / kNQ, c = (t - kPVS) % kNQ;
@@ -955,7 +964,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   pv_block(((n - 1) % kNS) * kVTSlotB, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no direct load may land after the workgroup ends
 
-  const float l_tot = xor32_sum(l_acc[0]);
+  // query j's normaliser: lane j % 16, element j / 16
+  const int l_src = (lane & 15) * 4;
+  const float l_lo = __int_as_float(__builtin_amdgcn_ds_bpermute(l_src, __float_as_int(l_acc[0])));
+  const float l_hi = __int_as_float(__builtin_amdgcn_ds_bpermute(l_src, __float_as_int(l_acc[1])));
+  const float l_tot = (j & 16) ? l_hi : l_lo;
   const float inv = 1.0f / l_tot;
   const int c_out = c_w + j;
   if (c_out < p.C) {
