@@ -101,10 +101,15 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Maximum that propagates NaN (llvm.maximum). Unlike fmaxf it needs no
+// quieting of its inputs first, and chains of it become three-input
+// v_maximum3_f32; a NaN score yields a NaN row either way.
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max / sum with the partner lane (lane ^ 32)
 __device__ __forceinline__ float xor32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -663,8 +668,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   float m_ref = -INFINITY;   // reference max (log2 domain) the exponentials subtract
   float m_use = 0.f;         // m_ref, or 0 while it is -inf
-  float pend = 1.f;          // factor O still owes (deferred rescale)
-  bool have_pend = false;    // wave-uniform
+  float m_old = -INFINITY;   // the reference before the latest decision
+  bool have_pend = false;    // wave-uniform: O and the normaliser owe exp2(m_old - m_use)
   const float sl = p.scale_log2;
   f32x16 sc[kSB];            // scores of one step (raw, then scaled and shifted)
   u32x4 pw[kSB][2];          // bf16 probabilities of one step, packed in pairs (P^T operands)
@@ -714,9 +719,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (32 * hb + perm_key(8 * (r >> 2) + (r & 3)) > lim) sc[hb][r] = -INFINITY;
   };
   auto max_block = [&](int hb) {
-    float m = fmaxf(sc[hb][0], sc[hb][1]);
+    float m = max_nan(sc[hb][0], sc[hb][1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) m = fmaxf(fmaxf(m, sc[hb][r]), sc[hb][r + 1]);
+    for (int r = 2; r < 16; r += 2) m = max_nan(max_nan(m, sc[hb][r]), sc[hb][r + 1]);
     return m;
   };
   auto scale_block = [&](int hb) {
@@ -735,24 +740,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       exp_pair(hb, 1, e);
     }
   };
-  // The reference decision for S(u), at the start of step u: mb0 (the
-  // maximum of S(u) keys 0-31) was taken in step u - 1, mb1 is taken here.
-  // Branch-free: without a move alpha is exactly 1.
-  float mb0_c = -INFINITY;
-  auto decide = [&](float mb1) {
-    const float mt = xor32_max(fmaxf(mb0_c, mb1)) * sl;
+  // The reference decision for S(u), at the start of step u, from m, this
+  // lane's maximum of S(u) (the partner lane holds the other half of the
+  // row). Branch-free; the factor itself is computed only when the
+  // reference moves, at the end of the step.
+  float mb0_c = -INFINITY;   // maximum of S(u) keys 0-31, taken in step u - 1
+  auto decide_max = [&](float m) {
+    const float mt = xor32_max(m) * sl;
     const bool need = __builtin_amdgcn_ballot_w64(mt > m_ref + kLazy) != 0;
-    const float m_new = need ? fmaxf(m_ref, mt) : m_ref;
-    const float alpha = fast_exp2(m_ref - ((m_new == -INFINITY) ? 0.f : m_new));
-    pend = alpha;
-    have_pend = need;
-    m_ref = m_new;
+    m_old = m_ref;
+    m_ref = need ? max_nan(m_ref, mt) : m_ref;
     m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    have_pend = need;
   };
+  auto decide = [&](float mb1) { decide_max(max_nan(mb0_c, mb1)); };
   // end of step u: O, now holding PV up to step u - 1 against the old
   // reference, takes the factor decided at the start of the step
   auto step_end = [&] {
     if (have_pend) {
+      const float pend = fast_exp2(m_old - m_use);
 #pragma unroll
       for (int db = 0; db < kNDB; ++db)
 #pragma unroll
@@ -849,16 +855,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[16 + (t - kPVS)], qf[c], c == 0 ? zero : sc[hb], 0, 0, 0);
       }
       // VALU in the MFMA's shadow
-      if (t == 0) {
-        mb0 = fmaxf(fmaxf(sc[1][0], sc[1][1]), sc[1][2]);   // maxima of S(u) keys 32-63, in mb0 until the decision
+      if (t < 2) {
+        // maxima of S(u) keys 32-63 joined to those of keys 0-31, three-input maxima
+        if (t == 0) mb0 = mb0_c;
 #pragma unroll
-        for (int r = 3; r < 9; r += 2) mb0 = fmaxf(fmaxf(mb0, sc[1][r]), sc[1][r + 1]);
-      } else if (t == 1) {
-#pragma unroll
-        for (int r = 9; r < 15; r += 2) mb0 = fmaxf(fmaxf(mb0, sc[1][r]), sc[1][r + 1]);
-        mb0 = fmaxf(mb0, sc[1][15]);
+        for (int r = 8 * t; r < 8 * t + 8; r += 2) mb0 = max_nan(max_nan(mb0, sc[1][r]), sc[1][r + 1]);
       } else if (t == 2) {
-        decide(mb0);
+        decide_max(mb0);
       } else if (t < 10) {
         // scalings: block 0 in slots 3-6, block 1 elements 0-11 in slots 7-9
 #pragma unroll
@@ -877,12 +880,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int i = t - kPVS;
         exp_pair(1, i / 4, i % 4);
       } else if (t == kPVS + 9) {
-        mb0 = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
+        mb0 = max_nan(max_nan(sc[0][0], sc[0][1]), sc[0][2]);
       } else if (t > kPVS + 9) {
-        const int r = 3 + 3 * (t - kPVS - 10);   // slots 30-34: elements 3-15
-#pragma unroll
-        for (int k2 = 0; k2 < 3; ++k2)
-          if (r + k2 < 16) mb0 = fmaxf(mb0, sc[0][r + k2]);
+        const int r = 3 + 2 * (t - kPVS - 10);   // slots 30-35: elements 3-14 in pairs, then 15
+        mb0 = max_nan(max_nan(mb0, sc[0][r]), sc[0][r + 1]);
+        if (r == 13) mb0 = max_nan(mb0, sc[0][15]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
