@@ -652,17 +652,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // takes the P^T operand register as its B operand. Read that way, lane
   // groups 0 and 2 (lanes 0-15, 32-47) hold the 16 keys of queries 0-15 in
   // their k positions, groups 1 and 3 those of queries 16-31. The A operand
-  // has ones where row 0 meets groups 0 and 2 and where row 1 meets groups 1
+  // has ones where row 0 meets groups 0 and 2 and where row 4 meets groups 1
   // and 3, zeros elsewhere, so row 0 of l_acc accumulates the sum over keys of
-  // the bf16 probabilities of queries 0-15 and row 1 that of queries 16-31
-  // (exact products, fp32 sums), in elements 0 and 1 of lanes 0-15. This
-  // needs only that A and B spread k over lanes and elements alike. l_acc is
-  // rescaled together with O.
+  // the bf16 probabilities of queries 0-15 and row 4 that of queries 16-31
+  // (exact products, fp32 sums). Rows 0 and 4 land in element 0 of lanes 0-15
+  // and 16-31: lane j holds query j's sum, the query whose reference and
+  // rescale factor it also holds; every other element is zero. This needs
+  // only that A and B spread k over lanes and elements alike.
   f32x4 l_acc = {0.f, 0.f, 0.f, 0.f};
   bf16x8 ones_row;
   {
     const int g = lane >> 4, r16 = lane & 15;
-    const bool one = (r16 == 0 && (g & 1) == 0) || (r16 == 1 && (g & 1) == 1);
+    const bool one = (r16 == 0 && (g & 1) == 0) || (r16 == 4 && (g & 1) == 1);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones_row[e] = one ? (__bf16)1.0f : (__bf16)0.0f;
   }
@@ -764,7 +765,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[db][r] *= pend;
       l_acc[0] *= pend;   // the other elements of l_acc stay 0
-      l_acc[1] *= pend;
       have_pend = false;
     }
   };
@@ -966,11 +966,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   pv_block(((n - 1) % kNS) * kVTSlotB, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no direct load may land after the workgroup ends
 
-  // query j's normaliser: lane j % 16, element j / 16
-  const int l_src = (lane & 15) * 4;
-  const float l_lo = __int_as_float(__builtin_amdgcn_ds_bpermute(l_src, __float_as_int(l_acc[0])));
-  const float l_hi = __int_as_float(__builtin_amdgcn_ds_bpermute(l_src, __float_as_int(l_acc[1])));
-  const float l_tot = (j & 16) ? l_hi : l_lo;
+  const float l_tot = xor32_sum(l_acc[0]);   // lanes 32-63 hold zeros in element 0
   const float inv = 1.0f / l_tot;
   const int c_out = c_w + j;
   if (c_out < p.C) {
