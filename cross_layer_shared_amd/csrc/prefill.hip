@@ -667,10 +667,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones_row[e] = one ? (__bf16)1.0f : (__bf16)0.0f;
   }
-  float m_ref = -INFINITY;   // reference max (log2 domain) the exponentials subtract
-  float m_use = 0.f;         // m_ref, or 0 while it is -inf
-  float m_old = -INFINITY;   // the reference before the latest decision
-  bool have_pend = false;    // wave-uniform: O and the normaliser owe exp2(m_old - m_use)
+  // Reference max (log2 domain) the exponentials subtract. It starts at the
+  // most negative finite value, so the first finite score moves it before
+  // any exponential and masked (-inf) scores still give exp2(-inf) = 0.
+  float m_ref = -__FLT_MAX__;
+  float m_old = -__FLT_MAX__;   // the reference before the latest decision
+  bool have_pend = false;       // wave-uniform: O and the normaliser owe exp2(m_old - m_ref)
   const float sl = p.scale_log2;
   f32x16 sc[kSB];            // scores of one step (raw, then scaled and shifted)
   u32x4 pw[kSB][2];          // bf16 probabilities of one step, packed in pairs (P^T operands)
@@ -727,7 +729,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   auto scale_block = [&](int hb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_use);
+    for (int r = 0; r < 16; ++r) sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_ref);
   };
   // exponentials of two scaled scores, rounded to a bf16 pair in pw (the
   // normaliser sums exactly these rounded values, in l_acc)
@@ -751,7 +753,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const bool need = __builtin_amdgcn_ballot_w64(mt > m_ref + kLazy) != 0;
     m_old = m_ref;
     m_ref = need ? max_nan(m_ref, mt) : m_ref;
-    m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     have_pend = need;
   };
   auto decide = [&](float mb1) { decide_max(max_nan(mb0_c, mb1)); };
@@ -759,7 +760,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // reference, takes the factor decided at the start of the step
   auto step_end = [&] {
     if (have_pend) {
-      const float pend = fast_exp2(m_old - m_use);
+      const float pend = fast_exp2(m_old - m_ref);
 #pragma unroll
       for (int db = 0; db < kNDB; ++db)
 #pragma unroll
@@ -867,13 +868,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * (t - 3) + i, hb = e / 16, r = e % 16;
-          sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_use);
+          sc[hb][r] = __builtin_fmaf(sc[hb][r], sl, -m_ref);
         }
       } else if (t < 18) {
         // exponentials of keys 0-31 (P(u - 1) keys 0-31 was read by slot 9);
         // block 1 elements 12-15 scaled in slots 10-13
         const int i = t - 10;
-        if (i < 4) sc[1][12 + i] = __builtin_fmaf(sc[1][12 + i], sl, -m_use);
+        if (i < 4) sc[1][12 + i] = __builtin_fmaf(sc[1][12 + i], sl, -m_ref);
         exp_pair(0, i / 4, i % 4);
       } else if (t >= kPVS && t < kPVS + 8) {
         // exponentials of keys 32-63 (P(u - 1) keys 32-63 was read by slot 19)
