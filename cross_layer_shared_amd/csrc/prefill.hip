@@ -490,8 +490,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // Software-pipelined kernel (D = 128). A SIMD's matrix core and its vector
 // ALU overlap well only when one wavefront interleaves both kinds of
 // instruction: a wavefront issuing MFMAs back to back leaves the other
-// wavefront of its SIMD few VALU issue slots, whereas VALU instructions placed
-// between a wavefront's own independent MFMAs run in their shadow. So every
+// wavefront of its SIMD few VALU issue slots (and of two wavefronts with an
+// MFMA ready, the older always gets the matrix core), whereas VALU
+// instructions placed between a wavefront's own MFMAs run in their shadow. So every
 // wavefront runs the whole pipeline itself, in 64-key steps. Step u, with the
 // scores S(u) and the probabilities P(u - 1) in registers, is 36 MFMA slots,
 // each an MFMA and the VALU work it shadows, fenced so the compiler keeps the
@@ -529,8 +530,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // transposes V step u + 1 into V^T slot (u + 1) % 3 (last read by PV in step
 // u - 1), reads K slot (u + 1) % 3 and V^T slot (u - 1) % 3. Before the
 // barrier that ends step u each wavefront waits for all its loads but the four
-// just issued and for its LDS accesses. Rows past the cache prefix lie outside
-// the buffer range and load as zeros.
+// just issued; the LDS reads it may still have in flight are the next step's
+// first operands, from a V^T slot not rewritten before step u + 2. Rows past
+// the cache prefix lie outside the buffer range and load as zeros.
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (vmcnt is split over bits 3:0 and 15:14) and leaves the other
 // counters unconstrained.
