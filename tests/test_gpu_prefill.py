@@ -156,15 +156,15 @@ def test_full_chunked_prefill_workload():
     _compare(o, lse, _oracle(q, k, v, 0, rows=rows), rows=rows)
 
 
-@pytest.mark.parametrize("D", [128, 64])
-def test_reference_moves_differ_between_queries(D):
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (128, 4, 2), (128, 4, 4), (64, 8, 2)])
+def test_reference_moves_differ_between_queries(D, Hq, Hkv):
     """Key rows scaled by 4 to 32 (exact powers of two) before and inside the
     chunk make each query's running maximum jump several times, by amounts and
     at steps that differ between the queries of one wavefront (the sign of
     each query's product with a scaled row is its own), so the lazy rescale of
     the numerator and the normaliser runs with a separate factor per query.
     The other cases rarely move the reference after its first value."""
-    B, Hq, Hkv, p0, C = 1, 8, 2, 700, 300
+    B, p0, C = 1, 700, 300
     w = S.Workload("pf_moves", 77, B=B, T=p0 + C, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16")
     k, v = S.cache_kv(w)
     for f, rows in [(4, [90, 400]), (8, [250, 760]), (16, [520, 880]), (32, [690, 950])]:
