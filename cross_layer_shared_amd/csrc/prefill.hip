@@ -288,20 +288,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     float mb[kNB];
 #pragma unroll
     for (int hb = 0; hb < kNB; ++hb) {
-      float m = fmaxf(sc[hb][0], sc[hb][1]);
+      float m = max_nan(sc[hb][0], sc[hb][1]);
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) m = fmaxf(fmaxf(m, sc[hb][r]), sc[hb][r + 1]);
+      for (int r = 2; r < 16; r += 2) m = max_nan(max_nan(m, sc[hb][r]), sc[hb][r + 1]);
       mb[hb] = m;
     }
     // the scale is positive, so the max of the scaled scores is the scaled max
-    const float mt = xor32_max(fmaxf(fmaxf(mb[0], mb[1]), fmaxf(mb[2], mb[3]))) * sl;
+    const float mt = xor32_max(max_nan(max_nan(mb[0], mb[1]), max_nan(mb[2], mb[3]))) * sl;
     // Lazy rescaling: the reference max m_run only moves when some row's
     // tile max exceeds it by more than kLazy (log2 units), so exponentials
     // stay below 2^kLazy and the accumulators are rescaled in few tiles.
     // Numerator and normaliser share the reference, so the result is exact
     // up to rounding for any choice of it.
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mt);
+      const float m_new = max_nan(m_run, mt);
       const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
       l_run *= alpha;
 #pragma unroll
