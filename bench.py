@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--cpu-units", action="store_true", help="also time the oracle on one unit of each other workload")
+    ap.add_argument("--clock-seconds", type=float, default=1.5,
+                    help="seconds of back-to-back prefill during which the engine clock is sampled (0: skip)")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of each non-headline leg")
     ap.add_argument("--decode-splits", type=int, default=0, help="split count of the headline decodes (0: automatic)")
     ap.add_argument("--long-splits", type=int, default=0, help="split count of the long-context decodes (0: automatic)")
@@ -300,6 +302,73 @@ def leg_compose_backward(args, torch, Y, S):
             "gbs": nbytes / ms / 1e6, "best_gbs": nbytes / best / 1e6, "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBS}
 
 
+class ClockSampler:
+    """Samples the engine (GFX) clock of each XCD and the socket power of the
+    GPU that runs cuda:0 through the amdsmi library, every 20 ms, on a thread,
+    from `settle` seconds after the start (the clock ramps up from idle first).
+    The dense bf16 peak assumes 2.4 GHz; the clock a box holds under sustained
+    matrix-core load is lower, and this records it."""
+
+    def __init__(self, torch, settle: float = 0.25):
+        import threading
+        import amdsmi
+        self.smi, self.samples, self.stop = amdsmi, [], threading.Event()
+        self.settle, self.t0 = settle, 0.0
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if not handles:
+            raise RuntimeError("amdsmi sees no GPU")
+        self.handle = handles[0]
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        if bus is not None and len(handles) > 1:
+            for h in handles:
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                    self.handle = h
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+            power = m.get("current_socket_power")
+            if clks and time.perf_counter() - self.t0 >= self.settle:   # past the ramp from idle
+                self.samples.append((sum(clks) / len(clks), min(clks), max(clks),
+                                     power if isinstance(power, (int, float)) else None))
+            self.stop.wait(0.02)
+
+    def __enter__(self):
+        self.t0 = time.perf_counter()
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join()
+        self.smi.amdsmi_shut_down()
+
+
+def clocked_window(torch, fn, seconds: float) -> dict:
+    """Run fn back to back for about `seconds` while sampling the engine clock;
+    returns the clock and power medians and the time per call in the window."""
+    import statistics
+    calls = 0
+    with ClockSampler(torch) as smp:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            fn()
+            calls += 1
+            torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / calls
+    if not smp.samples:
+        raise RuntimeError("no clock samples")
+    mean_mhz = [x[0] for x in smp.samples]
+    power = [x[3] for x in smp.samples if x[3] is not None]
+    return {"calls": calls, "ms_per_call": ms, "samples": len(smp.samples),
+            "gfxclk_mhz_median": statistics.median(mean_mhz),
+            "gfxclk_mhz_min_xcd": min(x[1] for x in smp.samples), "gfxclk_mhz_max_xcd": max(x[2] for x in smp.samples),
+            "socket_power_w_median": statistics.median(power) if power else None}
+
+
 def leg_prefill(args, torch, Y, S):
     w = S.PREFILL_CHUNKED
     B, T, Hq, Hkv, D, C = w.B, w.T, w.Hq, w.Hkv, w.D, w.chunk
@@ -317,7 +386,7 @@ def leg_prefill(args, torch, Y, S):
     ms, best = timed(torch, run, max(2, args.reps // 2))
     flop = 4.0 * B * Hq * D * T * (T + 1) / 2
     # the same 8 chunk launches captured once in a HIP graph (no host launch gaps)
-    graph_tflops, graph_note = None, None
+    graph_tflops, graph_note, graph = None, None, None
     try:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -326,13 +395,24 @@ def leg_prefill(args, torch, Y, S):
         torch.cuda.synchronize()
         gms, _ = timed(torch, graph.replay, max(2, args.reps // 2))
         graph_tflops = flop / gms / 1e9
-        del graph
     except RuntimeError as e:   # reported; the eager figure stands
-        graph_note = f"graph capture failed: {e}"
+        graph_note, graph = f"graph capture failed: {e}", None
+    # the engine clock the box holds while the prefill runs back to back
+    clock = None
+    if args.clock_seconds > 0:
+        try:
+            clock = clocked_window(torch, graph.replay if graph is not None else run, args.clock_seconds)
+            clock["tflops"] = flop / clock["ms_per_call"] / 1e9
+            mhz = clock["gfxclk_mhz_median"]
+            clock["peak_at_clock_tflops"] = BF16_MFMA_PEAK_TFLOPS * mhz / 2400.0
+            clock["mfma_frac_at_clock"] = clock["tflops"] / clock["peak_at_clock_tflops"]
+        except Exception as e:   # noqa: BLE001 - the clock is context, never a reason to fail the bench
+            clock = {"note": f"clock not sampled: {type(e).__name__}: {e}"}
+    del graph
     return {"workload": "prefill_chunked (T=32768, chunk 4096, 32/8 heads, D=128, bf16)", "flop": flop,
             "ms": ms, "tflops": flop / ms / 1e9, "best_tflops": flop / best / 1e9,
             "mfma_frac": flop / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, "graph_tflops": graph_tflops,
-            "graph_note": graph_note}
+            "graph_note": graph_note, "clock": clock}
 
 
 def leg_long_decode(args, torch, Y, S, w, planted=False):
