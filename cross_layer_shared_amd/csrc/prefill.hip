@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 
 #include "common.h"
+#include "prefill_layout.h"
 
 namespace yoco {
 namespace {
@@ -92,7 +93,7 @@ __device__ __forceinline__ s16x4 read_tr16_scoped(const __bf16* __restrict__ p) 
 }
 
 // Row of a 32-key block that MFMA row i carries: bits 2 and 3 swapped.
-__device__ __forceinline__ int perm_key(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+using pipe::perm_key;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -540,21 +541,22 @@ constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 template <int HPW, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_pipe_kernel(PrefillParams p) {
-  constexpr int D = 128;
+  // LDS layout and per-lane addresses: prefill_layout.h (checked by a host build)
+  constexpr int D = pipe::kD;
   constexpr int WQ = kWaves / HPW;
-  constexpr int kSK = 64;                  // keys per step
+  constexpr int kSK = pipe::kSK;           // keys per step
   constexpr int kSB = kSK / 32;            // 32-key MFMA blocks per step
   constexpr int kNQ = D / 16, kNDB = D / 32;
-  constexpr int kNS = 3;                   // LDS slots per tensor
-  constexpr int kRowB = D * 2;             // bytes per stored K or V row
-  constexpr int kSlotB = kSK * kRowB;      // 16 KiB
-  constexpr int kVBase = kNS * kSlotB;     // V slots follow the K slots
-  constexpr int kVTRow = kSK * 2 + 16;     // bytes per V^T row (64 keys + pad)
-  constexpr int kVTSlotB = D * kVTRow;     // 18 KiB
-  constexpr int kVTBase = 2 * kNS * kSlotB;
-  constexpr int kLoads = kSK / 4 / kWaves; // direct loads (4 rows each) per wavefront, tensor and step
+  constexpr int kNS = pipe::kNS;           // LDS slots per tensor
+  constexpr int kRowB = pipe::kRowB;
+  constexpr int kSlotB = pipe::kSlotB;
+  constexpr int kVBase = pipe::kVBase;
+  constexpr int kVTRow = pipe::kVTRow;
+  constexpr int kVTSlotB = pipe::kVTSlotB;
+  constexpr int kLoads = pipe::kLoads;
   constexpr int kBufWord3 = 0x00020000;    // raw buffer resource, 32-bit data format
-  __shared__ __attribute__((aligned(16))) char lds[kVTBase + kNS * kVTSlotB];   // 150 KiB
+  static_assert(kWaves == pipe::kWaves, "one wavefront count");
+  __shared__ __attribute__((aligned(16))) char lds[pipe::kLdsBytes];   // 150 KiB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -608,9 +610,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   uint32_t koff[kLoads], voff[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    const int r = 8 * wave + 4 * i + (lane >> 4), ps = lane & 15;
-    koff[i] = (uint32_t)(r * kst_b) + 16u * (uint32_t)(ps ^ (r & 15));
-    voff[i] = (uint32_t)(r * vst_b) + 16u * (uint32_t)(ps ^ (4 * (r & 3)));
+    const int r = pipe::load_row(wave, i, lane), ps = lane & 15;
+    koff[i] = (uint32_t)(r * kst_b) + 16u * (uint32_t)pipe::k_load_chunk(r, ps);
+    voff[i] = (uint32_t)(r * vst_b) + 16u * (uint32_t)pipe::v_load_chunk(r, ps);
   }
   auto issue = [&](const char* base, int64_t st_b, const uint32_t* off, int x, int slot_byte) {
     const int rows = min(kv_len - kSK * x, kSK);
@@ -620,30 +622,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds + slot_byte + (8 * wave + 4 * i) * kRowB), 16, off[i], 0, 0, 0);
+          rs, (__attribute__((address_space(3))) void*)(lds + slot_byte + pipe::load_lds_offset(wave, i)), 16, off[i], 0,
+          0, 0);
   };
   auto issue_k = [&](int x, int slot) { issue(kb, kst_b, koff, x, slot * kSlotB); };
   auto issue_v = [&](int x, int slot) { issue(vb, vst_b, voff, x, kVBase + slot * kSlotB); };
 
   // LDS addresses (bytes). K operand of k-step c at aK[c] (+ slot, + 32-key block).
-  const int pk = perm_key(j);
-  const uint32_t aK0 = (uint32_t)(pk * kRowB + 16 * (q ^ (pk & 15)));
   uint32_t aK[kNQ];
 #pragma unroll
-  for (int c = 0; c < kNQ; ++c) aK[c] = aK0 ^ (32u * c);
-  // Transposing reads of a V tile: wavefront w covers keys kb_w .. +4 and kb_w + 8 .. +4
-  // (kb_w = 16 (w / 2) + 4 (w % 2)) of all 128 dims, one read per 32-dim block; lane
-  // (gq, i) of a read receives dim 16 (gq % 2) + i of 4 consecutive keys.
-  const int gq = lane >> 4, sl16 = lane & 15, r4 = sl16 >> 2;
-  const int kb_w = 16 * (wave >> 1) + 4 * (wave & 1);
-  const uint32_t aT0 = (uint32_t)(kVBase + (kb_w + 8 * (gq >> 1) + r4) * kRowB + 64 * r4 + 32 * (gq & 1) +
-                                  16 * ((sl16 >> 1) & 1) + 8 * (sl16 & 1));
+  for (int c = 0; c < kNQ; ++c) aK[c] = pipe::k_operand(lane, c);
+  // Transposing reads of a V tile (wavefront w covers 8 keys of all 128 dims, one
+  // read per 32-dim block), where their 4 keys land in V^T, and where lane l
+  // reads its PV operand (dim l % 32, keys 8 (l / 32) .. +8).
   uint32_t aT[kNDB];
 #pragma unroll
-  for (int db = 0; db < kNDB; ++db) aT[db] = aT0 ^ (64u * db);
-  // where those 4 keys land in V^T, and where lane l reads its PV operand (dim l % 32, keys 8 (l / 32) .. +8)
-  const uint32_t aW = (uint32_t)(kVTBase + (16 * (gq & 1) + sl16) * kVTRow + 2 * (kb_w + 8 * (gq >> 1)));
-  const uint32_t aP = (uint32_t)(kVTBase + j * kVTRow + 16 * q);
+  for (int db = 0; db < kNDB; ++db) aT[db] = pipe::tr_read(wave, lane, db);
+  const uint32_t aW = pipe::vt_write(wave, lane, 0);
+  const uint32_t aP = pipe::pv_operand(lane, 0, 0, 0);
 
   f32x16 o_acc[kNDB];
 #pragma unroll

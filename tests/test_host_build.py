@@ -6,7 +6,12 @@
   YOCO_ERR_LAUNCH, rejected calls launch nothing, and the decode's 32-bit row
   offsets hold at the largest accepted cache length (tests/host_build/abi_driver.cpp);
 - the division by invariant integers the streaming kernels use
-  (tests/host_build/fastdiv_check.cpp), against plain division.
+  (tests/host_build/fastdiv_check.cpp), against plain division;
+- every LDS address the pipelined prefill forms (prefill_layout.h, through
+  tests/host_build/prefill_layout_check.cpp): slot bounds, that the direct
+  loads fill each tile once, that each MFMA operand read finds the rows and
+  dims its lane supplies, and the bank-conflict-free reads; planted mistakes in
+  a copy of the layout make that check fail.
 
 The host compiler is g++ (the C ABI layer includes only the HIP runtime's API
 header), so no device code is built here."""
@@ -50,3 +55,34 @@ def test_fastdiv_equals_division(tmp_path):
     # fastdiv.h is included by the kernels too; its host path needs only the HIP host macros
     _build_and_run(tmp_path, "fastdiv_check", [os.path.join(HERE, "fastdiv_check.cpp")],
                    ["-O2", "-include", "hip/hip_runtime.h"])
+
+
+def test_prefill_lds_addresses(tmp_path):
+    _build_and_run(tmp_path, "prefill_layout_check", [os.path.join(HERE, "prefill_layout_check.cpp")],
+                   ["-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"])
+
+
+# plausible slips in the layout, each of which the check must reject
+LAYOUT_MUTATIONS = {
+    "V rows loaded without their swizzle": ("return pos ^ (4 * (row & 3));", "return pos;"),
+    "K operand chunk not swizzled by its row": ("16 * (q ^ (pk & 15))", "16 * q"),
+    "K operand rows in plain order": ("pk = perm_key(j);", "pk = j;"),
+    "transposing read without the row's chunk swizzle": ("* kRowB + 64 * r4 +", "* kRowB +"),
+    "V^T write column in elements, not bytes": ("kVTRow + 2 * tr_first_key(wave, lane)", "kVTRow + tr_first_key(wave, lane)"),
+    "PV operand keys of the wrong half": ("+ 16 * q + db * 32 * kVTRow", "+ 16 * (1 - q) + db * 32 * kVTRow"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYOUT_MUTATIONS))
+def test_prefill_lds_address_check_rejects_planted_mistakes(tmp_path, name):
+    old, new = LAYOUT_MUTATIONS[name]
+    text = open(os.path.join(CSRC, "prefill_layout.h")).read()
+    assert text.count(old) == 1, old
+    (tmp_path / "prefill_layout.h").write_text(text.replace(old, new))
+    src = tmp_path / "prefill_layout_check.cpp"     # next to the mutated header, which it then includes
+    src.write_text(open(os.path.join(HERE, "prefill_layout_check.cpp")).read())
+    exe = str(tmp_path / "check")
+    r = subprocess.run(["g++", *COMMON, "-O1", str(src), "-o", exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert run.returncode != 0 and "FAIL" in run.stdout, f"{name}: not detected\n{run.stdout[-1000:]}"
