@@ -587,14 +587,16 @@ def leg_early_exit(args, torch, Y, S):
             "speedup": full_ms / ee_ms, "max_abs_last_row_decode_vs_prefill": agree}
 
 
-def leg_ceiling(args, torch):
+def leg_ceiling(args, torch, S):
     """Achievable-bandwidth probes (libyoco_ceiling.so), timed like the kernels they
     bound (back-to-back launches in a HIP graph): a plain streaming read of 128 MiB
     (the mid-context decode's cache; rotating over 8 buffers so that the Infinity
     Cache serves none of it, and on one buffer, which it serves) and of 2 GiB (the
     long decodes' caches), and the compose's four-reads-two-writes traffic at its
     384 MiB per call (rotating over 3 buffer sets), each over several launch
-    shapes; the best median of each is the ceiling of the matching kernel."""
+    shapes; the best median of each is the ceiling of the matching kernel. And
+    the matrix cores' sustained bf16 MFMA rate on N(0,1) and on zero operands,
+    the ceiling of the prefill."""
     from cross_layer_shared_amd import ceiling as C
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     res = {}
@@ -641,6 +643,34 @@ def leg_ceiling(args, torch):
     out["hbm"] = best(out, "hbm")
     res["read4_write2_384MiB"] = out
     del sets
+    # matrix cores: back-to-back bf16 MFMAs (the prefill's instruction) on N(0,1)
+    # operands, the prefill workload's data, and on zeros; the rate the chip
+    # sustains depends on the operand values, so both are timed, each over the
+    # same clock-sampled window as the prefill
+    pool = {"normal": up(S.normal_bf16(S.PREFILL_CHUNKED.seed, (0x4D46,), (1 << 20,)), torch),
+            "zeros": torch.zeros(1 << 20, dtype=torch.bfloat16, device="cuda")}
+    fsink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    wg, iters = 256, 16384
+    flop = C.mfma_flop(wg, iters)
+    out = {"instruction": "v_mfma_f32_32x32x16_bf16", "workgroups": wg, "waves_per_simd": 2, "iters": iters,
+           "flop_per_call": flop}
+    for name, buf in pool.items():
+        fn = lambda buf=buf: C.yoco_ceiling_mfma_bf16(buf, fsink, wg, iters)  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        row = {}
+        if args.clock_seconds > 0:
+            try:
+                row = clocked_window(torch, fn, args.clock_seconds)
+            except Exception as e:   # noqa: BLE001 - the clock is context; time the calls without it
+                row = {"clock_note": f"clock not sampled: {type(e).__name__}: {e}"}
+        if "ms_per_call" not in row:
+            row["ms_per_call"], _ = timed(torch, fn, args.reps)
+        row["tflops"] = flop / row["ms_per_call"] / 1e9
+        row["frac_of_peak"] = row["tflops"] / BF16_MFMA_PEAK_TFLOPS
+        out[name] = row
+    res["mfma_bf16"] = out
+    del pool
     return res
 
 
@@ -749,7 +779,7 @@ def main():
     h = headline(args, torch, Y, S)
     extra = {}
     if "ceiling" in legs:
-        extra["ceiling"] = leg_ceiling(args, torch)
+        extra["ceiling"] = leg_ceiling(args, torch, S)
     if "compose" in legs:
         extra["compose"] = leg_compose(args, torch, Y, S)
     if "backward" in legs:
@@ -777,6 +807,10 @@ def main():
         for k in ("decode_long_context", "decode_million_token"):
             if k in extra:
                 vs[k] = extra[k]["gbs"] / c["read_2GiB"]["hbm"]["gbs"]
+        if "prefill" in extra:   # both from back-to-back windows of the same length
+            pf = extra["prefill"]
+            pf_tflops = (pf.get("clock") or {}).get("tflops") or pf["tflops"]
+            vs["prefill_vs_mfma_on_normal_operands"] = pf_tflops / c["mfma_bf16"]["normal"]["tflops"]
         c["fraction_of_ceiling"] = vs
 
     w = S.DECODE_MID

@@ -1,7 +1,8 @@
-"""Python binding of libyoco_ceiling.so (achievable-bandwidth probes): argument
+"""Python binding of libyoco_ceiling.so (achievable-rate probes): argument
 marshalling only, like the binding of libyoco.so. The probes are plain
 streaming kernels with the traffic pattern of the decode (one read of a buffer)
-and of the compose (four reads, two writes) and none of the method's
+and of the compose (four reads, two writes), and back-to-back bf16 MFMAs on
+caller-supplied operands for the prefill, with none of the method's
 arithmetic; the benchmark times them beside the kernels they bound."""
 from __future__ import annotations
 
@@ -14,7 +15,8 @@ from .binding import YocoError, _stream
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 CEILING_LIB_PATH = os.path.join(_HERE, "libyoco_ceiling.so")
-CEILING_EXPORTED = ("yoco_ceiling_read", "yoco_ceiling_read4_write2", "yoco_ceiling_last_error")
+CEILING_EXPORTED = ("yoco_ceiling_read", "yoco_ceiling_read4_write2", "yoco_ceiling_mfma_bf16",
+                    "yoco_ceiling_last_error")
 
 _lib = None
 
@@ -32,6 +34,8 @@ def load_ceiling_library(path: str = CEILING_LIB_PATH) -> ctypes.CDLL:
     lib.yoco_ceiling_read.restype = i
     lib.yoco_ceiling_read4_write2.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, vp]
     lib.yoco_ceiling_read4_write2.restype = i
+    lib.yoco_ceiling_mfma_bf16.argtypes = [vp, sz, i, i, vp, vp]
+    lib.yoco_ceiling_mfma_bf16.restype = i
     lib.yoco_ceiling_last_error.argtypes = []
     lib.yoco_ceiling_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -65,3 +69,21 @@ def yoco_ceiling_read4_write2(a, b, c, d, e, f, threads: int = 512, stream=None)
     _check(load_ceiling_library().yoco_ceiling_read4_write2(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
                                                             e.data_ptr(), f.data_ptr(), n, int(threads),
                                                             _stream(stream)))
+
+
+MFMA_THREADS = 512
+MFMA_FLOP = 32 * 32 * 16 * 2      # one v_mfma_f32_32x32x16_bf16
+
+
+def mfma_flop(workgroups: int, iters: int) -> float:
+    """Floating-point operations of one yoco_ceiling_mfma_bf16 call."""
+    return float(workgroups) * (MFMA_THREADS // 64) * iters * 16 * MFMA_FLOP
+
+
+def yoco_ceiling_mfma_bf16(operands: torch.Tensor, sink: torch.Tensor, workgroups: int = 256, iters: int = 4096,
+                           stream=None) -> None:
+    """Back-to-back bf16 MFMAs on operands from the bf16 pool `operands`; sink is a device float32 [>= 1]."""
+    if operands.dtype != torch.bfloat16:
+        raise ValueError("operands must be bfloat16")
+    _check(load_ceiling_library().yoco_ceiling_mfma_bf16(operands.data_ptr(), _nbytes(operands), int(workgroups),
+                                                         int(iters), sink.data_ptr(), _stream(stream)))

@@ -1,10 +1,11 @@
-// Achievable-bandwidth probes (libyoco_ceiling.so): plain streaming kernels
+// Achievable-rate probes (libyoco_ceiling.so): plain streaming kernels
 // with the traffic pattern of the decode (one read of a buffer, 16-byte loads,
 // several in flight per thread) and of the compose (four input streams, two
 // output streams, one 16-byte vector of each per thread), and none of the
 // method's arithmetic. The YOCO++ technical summary, section 3, prices decode
 // and composition in bytes moved; these kernels give the time those bytes take
-// on this chip when nothing else is done with them.
+// on this chip when nothing else is done with them. A matrix-core probe does the
+// same for the compute-bound prefill: back-to-back bf16 MFMAs on caller data.
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -71,6 +72,41 @@ __global__ __launch_bounds__(1024) void read4_write2_kernel(const u32x4* __restr
   const u32x4 vc = __builtin_nontemporal_load(c + i), vd = __builtin_nontemporal_load(d + i);
   __builtin_nontemporal_store(va + vb, e + i);
   __builtin_nontemporal_store(vc + vd, f + i);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kMfmaThreads = 512;     // 8 wavefronts: two per SIMD
+constexpr float kMfmaSinkKey = 1234.5f;
+
+// Matrix-core probe: two accumulators, each MFMA with a different (A, B) pair
+// from the 8 + 8 operand registers (A index r or r + 4, B index 3r + 1 or
+// 5r + 2, mod 8), so the operands change at every instruction as they do in
+// the prefill. A chain of 32x32x16 MFMAs on one accumulator issues at the
+// full rate, so two chains keep the matrix core busy.
+__global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const bf16x8* __restrict__ pool, uint32_t pool_vecs,
+                                                            int iters, float* __restrict__ sink) {
+  const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t base = (uint32_t)((16 * t) % pool_vecs);   // pool_vecs >= 16: one wrap at most
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t ia = base + r, ib = base + 8 + r;
+    a[r] = pool[ia >= pool_vecs ? ia - pool_vecs : ia];
+    b[r] = pool[ib >= pool_vecs ? ib - pool_vecs : ib];
+  }
+  f32x16 c0 = {}, c1 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b[(3 * r + 1) & 7], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(r + 4) & 7], b[(5 * r + 2) & 7], c1, 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += c0[e] + c1[e];
+  if (s == kMfmaSinkKey) sink[0] = s;
 }
 
 thread_local char g_err[256] = "";
@@ -149,6 +185,20 @@ yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* 
       static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), static_cast<const u32x4*>(c),
       static_cast<const u32x4*>(d), static_cast<u32x4*>(e), static_cast<u32x4*>(f), n);
   return launched("ceiling read4_write2");
+}
+
+yoco_status yoco_ceiling_mfma_bf16(const void* operands, size_t operand_bytes, int workgroups, int iters,
+                                   float* sink, hipStream_t stream) {
+  if (!operands || !sink) return fail(YOCO_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(operands)) return fail(YOCO_ERR_ALIGNMENT, "operands not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "sink not 4-byte aligned");
+  if (operand_bytes < 256 || operand_bytes % 16 || operand_bytes / 16 > 0xFFFFFFF0ull)
+    return fail(YOCO_ERR_INVALID_ARG, "operand_bytes must be a multiple of 16, at least 256 and below 2^36");
+  if (workgroups < 1 || workgroups > 65536) return fail(YOCO_ERR_INVALID_ARG, "workgroups must be 1..65536");
+  if (iters < 1 || iters > (1 << 24)) return fail(YOCO_ERR_INVALID_ARG, "iters must be 1..2^24");
+  mfma_kernel<<<dim3(workgroups), kMfmaThreads, 0, stream>>>(static_cast<const bf16x8*>(operands),
+                                                             (uint32_t)(operand_bytes / 16), iters, sink);
+  return launched("ceiling mfma_bf16");
 }
 
 }  // extern "C"

@@ -1,6 +1,7 @@
 /*
- * yoco_ceiling.h - achievable-bandwidth probes of MI355X (gfx950), the
- * yardsticks the HBM-bound kernels of libyoco.so are measured against.
+ * yoco_ceiling.h - achievable-rate probes of MI355X (gfx950), the yardsticks
+ * the kernels of libyoco.so are measured against: bandwidth for the HBM-bound
+ * ones, matrix-core throughput for the prefill.
  *
  * The YOCO++ technical summary, section 3 (efficiency analysis), states the
  * method's cost in memory traffic: decoding reads exactly one KV set per layer,
@@ -55,6 +56,29 @@ yoco_status yoco_ceiling_read(const void* src, size_t bytes, int workgroups, int
  */
 yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* c, const void* d, void* e, void* f,
                                       size_t bytes, int threads, hipStream_t stream);
+
+/*
+ * yoco_ceiling_mfma_bf16 - the matrix cores' achievable rate on given operand
+ * data, the yardstick of the MFMA-bound prefill (the YOCO++ technical summary,
+ * section 3, calls prefill compute-bound). Every wavefront of `workgroups`
+ * workgroups of 8 wavefronts (two per SIMD, as the prefill runs) issues
+ * 16 * iters v_mfma_f32_32x32x16_bf16 (32,768 flop each) back to back on two
+ * fp32 accumulators, taking its operands from 8 A and 8 B registers per lane
+ * in a rotation that gives every MFMA a different operand pair; the matrix
+ * core's power, and with it the rate the chip sustains, depends on those
+ * values, so the caller supplies them.
+ *   operands        device bf16 pool, 16-byte aligned, a multiple of 16
+ *                   bytes, at least 256; lane t of the grid loads its 16
+ *                   registers from 16-byte vectors (16 t + r) mod
+ *                   (operand_bytes / 16), r = 0 .. 15.
+ *   workgroups      1 .. 65536 (256 fills each CU of an MI355X once).
+ *   iters           1 .. 2^24.
+ *   sink            device float [1]: written only if the accumulators sum to
+ *                   a fixed value (keeps the products live).
+ * Work per call: workgroups * 8 * iters * 16 * 32768 flop.
+ */
+yoco_status yoco_ceiling_mfma_bf16(const void* operands, size_t operand_bytes, int workgroups, int iters,
+                                   float* sink, hipStream_t stream);
 
 /* Message of the last failing call on this host thread ("" if none). */
 const char* yoco_ceiling_last_error(void);

@@ -299,6 +299,19 @@ def test_ceiling_probes_reject_bad_arguments():
         (lib.yoco_ceiling_read4_write2(*bufs[:4], bufs[0], bufs[5], 1 << 20, 512, None), INVALID),   # e aliases a
         (lib.yoco_ceiling_read4_write2(*bufs[:5], bufs[4] + 16, 1 << 20, 512, None), INVALID),       # e, f overlap
     ]
+    cases += [
+        (lib.yoco_ceiling_mfma_bf16(None, 1 << 20, 256, 16, sink, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 1 << 20, 256, 16, None, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE + 8, 1 << 20, 256, 16, sink, None), ALIGN),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 1 << 20, 256, 16, sink + 2, None), ALIGN),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 0, 256, 16, sink, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 24, 256, 16, sink, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 240, 256, 16, sink, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 1 << 20, 0, 16, sink, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 1 << 20, 65537, 16, sink, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 1 << 20, 256, 0, sink, None), INVALID),
+        (lib.yoco_ceiling_mfma_bf16(BASE, 1 << 20, 256, (1 << 24) + 1, sink, None), INVALID),
+    ]
     for got, want in cases:
         assert got == want
         assert lib.yoco_ceiling_last_error().decode()
