@@ -13,9 +13,17 @@
 // One workgroup per (sequence b, kv head g, split), as in the vector kernel,
 // whose merge of the wavefronts, split partials and fused log-sum-exp merge
 // it shares (finish_split). A wavefront takes blocks of 32 cache rows:
+//   K and V rows arrive by 16-byte loads of whole rows (four rows of 256
+//     bytes per instruction at D = 128), the access pattern that streams
+//     fastest: a load instruction that gathers 64-byte pieces of 16 rows, as
+//     an MFMA operand taken straight from memory would, moves 128 MiB about
+//     17% slower. Both go through the wavefront's own LDS buffers.
 //   S^T = K Q^T: two 16-row MFMA blocks by 16 query columns (the G heads of
-//     kv head g; columns G..15 are zero), D/32 k-steps each. Row r of block
-//     bb carries cache row 8 (r / 4) + 4 bb + (r % 4), so that lane (lg, q)
+//     kv head g; columns G..15 are zero), D/32 k-steps each, the K operand
+//     one 16-byte LDS read (K rows stored with their 16-byte chunks XOR-
+//     swizzled so that the 16 rows one read instruction serves sit in
+//     distinct banks). Row r of block bb carries cache row
+//     8 (r / 4) + 4 bb + (r % 4), so that lane (lg, q)
 //     ends up with the scores of query q for the 8 consecutive rows
 //     8 lg .. 8 lg + 7 of the block: exactly the P^T operand it supplies to
 //   O^T += V^T P^T: one MFMA per 16 dims, V^T read from LDS with the gfx950
@@ -52,6 +60,16 @@ __device__ __forceinline__ s16x4_t read_tr16(const __bf16* ptr) {
       (lds_s16x4_t*)(__attribute__((address_space(3))) void*)(const_cast<__bf16*>(ptr)));
 }
 
+// LDS position of 16-byte chunk c of K row r (r < 32) in a wavefront's K
+// buffer: c ^ k_swizzle(r). The 16 rows a score operand read serves,
+// 8 (i / 4) + 4 bb + (i % 4), i < 16, then land in distinct banks (distinct
+// chunk positions of a 256-byte row at D = 128; distinct (row parity, chunk)
+// pairs at D = 64), and so do the 16 lanes of a row-contiguous write.
+template <int D>
+__host__ __device__ constexpr int k_swizzle(int r) {
+  return D == 128 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | ((r >> 2) & 6));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {(__bf16)a, (__bf16)b};   // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
@@ -82,8 +100,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   constexpr int RPI = 64 / LPR;        // cache rows per V load instruction
   constexpr int NVI = kBlock / RPI;    // V load instructions per block
   constexpr int SV = NW * kBlock * VPAD * 2;          // bytes of the per-wavefront V buffers
+  constexpr int SK = NW * kBlock * D * 2;             // bytes of the per-wavefront K buffers
   constexpr int SM = NW * G * (D + 2) * 4;            // bytes of the wavefront merge
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SV > SM ? SV : SM];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SV + SK > SM ? SV + SK : SM];
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -141,19 +160,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
                             te > 0 ? (uint32_t)te * kst : 0u);
   const auto rv = rows_rsrc(static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh) * 2,
                             te > 0 ? (uint32_t)te * vst : 0u);
-  // K operand of score block bb: row lr carries cache row 8 (lr / 4) + 4 bb + lr % 4, dims 32 j + 8 lg.
-  uint32_t koff[2];
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) koff[bb] = (uint32_t)(8 * (lr >> 2) + 4 * bb + (lr & 3)) * kst + 16u * lg;
-  // V block loads: instruction i brings rows RPI i .. + RPI, lane -> row lane / LPR, dims 8 (lane % LPR).
+  // Block loads: instruction i brings rows RPI i .. + RPI, lane -> row lane / LPR, dims 8 (lane % LPR).
+  const uint32_t koff = (uint32_t)(lane / LPR) * kst + 16u * (lane % LPR);
   const uint32_t voff = (uint32_t)(lane / LPR) * vst + 16u * (lane % LPR);
 
-  auto load = [&](int base, bf16x8_t (&kr)[2][NQK], u32x4_t (&vr)[NVI]) {
+  auto load = [&](int base, u32x4_t (&kr)[NVI], u32x4_t (&vr)[NVI]) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int j = 0; j < NQK; ++j)
-        kr[bb][j] = __builtin_bit_cast(bf16x8_t, buffer_load<4>(rk, (uint32_t)base * kst + koff[bb] + 64u * j));
+    for (int i = 0; i < NVI; ++i) kr[i] = buffer_load<4>(rk, (uint32_t)(base + RPI * i) * kst + koff);
 #pragma unroll
     for (int i = 0; i < NVI; ++i) vr[i] = buffer_load<4>(rv, (uint32_t)(base + RPI * i) * vst + voff);
   };
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   // the compose kernel's arithmetic, so the products see exactly the values a
   // composed cache would hold.
   __amdgpu_buffer_rsrc_t rk1 = rk, rv1 = rv;
-  uint32_t k1st = kst, v1st = vst, koff1[2] = {koff[0], koff[1]}, voff1 = voff;
+  uint32_t k1st = kst, v1st = vst, koff1 = koff, voff1 = voff;
   if constexpr (COR) {
     k1st = (uint32_t)(p.k1.st * 2);
     v1st = (uint32_t)(p.v1.st * 2);
@@ -171,8 +184,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
                     te > 0 ? (uint32_t)te * k1st : 0u);
     rv1 = rows_rsrc(static_cast<const char*>(p.v1.ptr) + ((int64_t)b * p.v1.sb + (int64_t)g * p.v1.sh) * 2,
                     te > 0 ? (uint32_t)te * v1st : 0u);
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) koff1[bb] = (uint32_t)(8 * (lr >> 2) + 4 * bb + (lr & 3)) * k1st + 16u * lg;
+    koff1 = (uint32_t)(lane / LPR) * k1st + 16u * (lane % LPR);
     voff1 = (uint32_t)(lane / LPR) * v1st + 16u * (lane % LPR);
   }
   auto compose4 = [&](u32x4_t x1, u32x4_t xi, float c1, float c2, int terms) {
@@ -181,30 +193,28 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
     for (int w = 0; w < 4; ++w) r[w] = compose_dword<true>(x1[w], xi[w], c1, c2, terms);
     return r;
   };
-  auto load_composed = [&](int base, bf16x8_t (&kr)[2][NQK], u32x4_t (&vr)[NVI]) {
-    bf16x8_t k1r[2][NQK];
-    u32x4_t v1r[NVI];
+  auto load_composed = [&](int base, u32x4_t (&kr)[NVI], u32x4_t (&vr)[NVI]) {
+    u32x4_t k1r[NVI], v1r[NVI];
     load(base, kr, vr);
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int j = 0; j < NQK; ++j)
-        k1r[bb][j] = __builtin_bit_cast(bf16x8_t, buffer_load<4>(rk1, (uint32_t)base * k1st + koff1[bb] + 64u * j));
+    for (int i = 0; i < NVI; ++i) k1r[i] = buffer_load<4>(rk1, (uint32_t)(base + RPI * i) * k1st + koff1);
 #pragma unroll
     for (int i = 0; i < NVI; ++i) v1r[i] = buffer_load<4>(rv1, (uint32_t)(base + RPI * i) * v1st + voff1);
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int j = 0; j < NQK; ++j)
-        kr[bb][j] = __builtin_bit_cast(bf16x8_t, compose4(__builtin_bit_cast(u32x4_t, k1r[bb][j]),
-                                                          __builtin_bit_cast(u32x4_t, kr[bb][j]), p.cK1, p.cK2,
-                                                          p.termsK));
+    for (int i = 0; i < NVI; ++i) kr[i] = compose4(k1r[i], kr[i], p.cK1, p.cK2, p.termsK);
 #pragma unroll
     for (int i = 0; i < NVI; ++i) vr[i] = compose4(v1r[i], vr[i], p.cV1, p.cV2, p.termsV);
   };
 
   __bf16* sv = reinterpret_cast<__bf16*>(smem) + wave * kBlock * VPAD;
   const __bf16* tr0 = sv + (8 * lg + (lr >> 2)) * VPAD + 4 * (lr & 3);   // rows 8 lg + 0..3 of this lane's reads
+  // this wavefront's K buffer: kBlock rows of D, chunk c of row r at position c ^ k_swizzle(r)
+  __bf16* sk = reinterpret_cast<__bf16*>(smem + SV) + wave * kBlock * D;
+  const int krow_w = lane / LPR, kchunk_w = lane % LPR;   // what this lane's block loads carry: row RPI i + krow_w
+  // score operand of block bb, k-step j: row 8 (lr / 4) + 4 bb + lr % 4, chunk 4 j + lg
+  int krd[2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) krd[bb] = (8 * (lr >> 2) + 4 * bb + (lr & 3)) * D;
   f32x4_t o[NDB];
 #pragma unroll
   for (int n = 0; n < NDB; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -212,18 +222,28 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   float l_run = 0.f;         // this lane's share of the running sum of query lr
   const float sl = p.scale_log2;
 
-  auto block = [&](const bf16x8_t (&kr)[2][NQK], const u32x4_t (&vr)[NVI], int base) {
-    // V rows into this wavefront's LDS buffer (row-major, padded rows)
+  auto block = [&](const u32x4_t (&kr)[NVI], const u32x4_t (&vr)[NVI], int base) {
+    // K and V rows into this wavefront's LDS buffers (K swizzled, V padded rows)
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) {
+      const int r = RPI * i + krow_w;
+      *reinterpret_cast<u32x4_t*>(sk + r * D + 8 * (kchunk_w ^ k_swizzle<D>(r))) = kr[i];
+    }
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
       *reinterpret_cast<u32x4_t*>(sv + (RPI * i + lane / LPR) * VPAD + 8 * (lane % LPR)) = vr[i];
+    __builtin_amdgcn_wave_barrier();
     // S^T: lane (lg, q) gets the raw scores of query q for rows 8 lg + 4 bb + i
     f32x4_t sc[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
+      const int r = 8 * (lr >> 2) + 4 * bb + (lr & 3);
       sc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NQK; ++j) sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[bb][j], qf[j], sc[bb], 0, 0, 0);
+      for (int j = 0; j < NQK; ++j) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(sk + krd[bb] + 8 * ((4 * j + lg) ^ k_swizzle<D>(r)));
+        sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[j], sc[bb], 0, 0, 0);
+      }
     }
     if (base + kBlock > te) {   // rows past the split's end
 #pragma unroll
@@ -279,14 +299,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   if constexpr (COR) {
     // one register set (four raw streams per block), composed as it arrives
     for (; base < te; base += STEP) {
-      bf16x8_t kr[2][NQK];
-      u32x4_t vr[NVI];
+      u32x4_t kr[NVI], vr[NVI];
       load_composed(base, kr, vr);
       block(kr, vr, base);
     }
   } else if (base < te) {
-    bf16x8_t ka[2][NQK], kb[2][NQK];
-    u32x4_t va[NVI], vb[NVI];
+    u32x4_t ka[NVI], kb[NVI], va[NVI], vb[NVI];
     load(base, ka, va);
     while (true) {
       const int nb = base + STEP;
