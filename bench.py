@@ -594,7 +594,9 @@ def leg_ceiling(args, torch, S):
     Cache serves none of it, and on one buffer, which it serves) and of 2 GiB (the
     long decodes' caches), and the compose's four-reads-two-writes traffic at its
     384 MiB per call (rotating over 3 buffer sets), each over several launch
-    shapes; the best median of each is the ceiling of the matching kernel. And
+    shapes (workgroups x threads x loads in flight per thread for the reads,
+    threads striding over a workgroup's range or wavefronts taking blocks);
+    the best median of each is the ceiling of the matching kernel. And
     the matrix cores' sustained bf16 MFMA rate on N(0,1) and on zero operands,
     the ceiling of the prefill."""
     from cross_layer_shared_amd import ceiling as C
@@ -612,11 +614,19 @@ def leg_ceiling(args, torch, S):
     nb = 1 << 27
     bufs = [torch.empty(nb // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(8)]
     out = {"bytes": nb, "shapes": {}}
-    for wg, th in [(256, 512), (256, 1024), (512, 512), (1024, 256), (0, 512)]:
-        rd = lambda i, wg=wg, th=th: C.yoco_ceiling_read(bufs[i], sink, workgroups=wg, threads=th)  # noqa: E731
+    for wg, th, u in [(256, 512, 4), (256, 512, 8), (256, 512, 16), (256, 1024, 8), (512, 512, 8), (1024, 256, 8),
+                      (0, 512, 8)]:
+        rd = lambda i, wg=wg, th=th, u=u: C.yoco_ceiling_read(bufs[i], sink, workgroups=wg, threads=th,  # noqa: E731
+                                                              loads_per_thread=u)
         row = {"hbm": rate(nb, *graph_time(torch, [lambda i=i: rd(i % 8) for i in range(16)], args.reps)),
                "warm": rate(nb, *graph_time(torch, [lambda: rd(0)] * 16, args.reps))}
-        out["shapes"][f"{wg or 'stride'}x{th}"] = row
+        out["shapes"][f"{wg or 'stride'}x{th}x{u}"] = row
+    for wg, th, u in [(256, 512, 4), (256, 512, 8), (512, 512, 8), (1024, 256, 8)]:   # per-wavefront blocks
+        rd = lambda i, wg=wg, th=th, u=u: C.yoco_ceiling_read_blocks(bufs[i], sink, workgroups=wg,  # noqa: E731
+                                                                     threads=th, loads_per_thread=u)
+        row = {"hbm": rate(nb, *graph_time(torch, [lambda i=i: rd(i % 8) for i in range(16)], args.reps)),
+               "warm": rate(nb, *graph_time(torch, [lambda: rd(0)] * 16, args.reps))}
+        out["shapes"][f"blocks{wg}x{th}x{u}"] = row
     out["hbm"], out["warm"] = best(out, "hbm"), best(out, "warm")
     res["read_128MiB"] = out
     del bufs
@@ -624,10 +634,16 @@ def leg_ceiling(args, torch, S):
     nb = 1 << 31
     bufs = [torch.empty(nb // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(2)]
     out = {"bytes": nb, "shapes": {}}
-    for wg, th in [(256, 512), (512, 512), (1024, 512), (2048, 256)]:
-        rd = lambda i, wg=wg, th=th: C.yoco_ceiling_read(bufs[i], sink, workgroups=wg, threads=th)  # noqa: E731
-        out["shapes"][f"{wg}x{th}"] = {"hbm": rate(nb, *graph_time(torch, [lambda i=i: rd(i % 2) for i in range(4)],
-                                                                   max(3, args.reps // 2)))}
+    for wg, th, u in [(256, 512, 8), (512, 512, 4), (512, 512, 8), (512, 512, 16), (1024, 512, 8), (2048, 256, 8)]:
+        rd = lambda i, wg=wg, th=th, u=u: C.yoco_ceiling_read(bufs[i], sink, workgroups=wg, threads=th,  # noqa: E731
+                                                              loads_per_thread=u)
+        out["shapes"][f"{wg}x{th}x{u}"] = {"hbm": rate(nb, *graph_time(torch, [lambda i=i: rd(i % 2) for i in range(4)],
+                                                                       max(3, args.reps // 2)))}
+    for wg, th, u in [(512, 512, 8), (1024, 512, 8), (2048, 256, 8)]:   # per-wavefront blocks
+        rd = lambda i, wg=wg, th=th, u=u: C.yoco_ceiling_read_blocks(bufs[i], sink, workgroups=wg,  # noqa: E731
+                                                                     threads=th, loads_per_thread=u)
+        out["shapes"][f"blocks{wg}x{th}x{u}"] = {
+            "hbm": rate(nb, *graph_time(torch, [lambda i=i: rd(i % 2) for i in range(4)], max(3, args.reps // 2)))}
     out["hbm"] = best(out, "hbm")
     res["read_2GiB"] = out
     del bufs

@@ -15,8 +15,8 @@ from .binding import YocoError, _stream
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 CEILING_LIB_PATH = os.path.join(_HERE, "libyoco_ceiling.so")
-CEILING_EXPORTED = ("yoco_ceiling_read", "yoco_ceiling_read4_write2", "yoco_ceiling_mfma_bf16",
-                    "yoco_ceiling_last_error")
+CEILING_EXPORTED = ("yoco_ceiling_read", "yoco_ceiling_read_blocks", "yoco_ceiling_read4_write2",
+                    "yoco_ceiling_mfma_bf16", "yoco_ceiling_last_error")
 
 _lib = None
 
@@ -30,8 +30,10 @@ def load_ceiling_library(path: str = CEILING_LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is missing: build it with `python -m cross_layer_shared_amd.build`")
     lib = ctypes.CDLL(path)
     i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
-    lib.yoco_ceiling_read.argtypes = [vp, sz, i, i, i, vp, vp]
+    lib.yoco_ceiling_read.argtypes = [vp, sz, i, i, i, i, vp, vp]
     lib.yoco_ceiling_read.restype = i
+    lib.yoco_ceiling_read_blocks.argtypes = [vp, sz, i, i, i, vp, vp]
+    lib.yoco_ceiling_read_blocks.restype = i
     lib.yoco_ceiling_read4_write2.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, vp]
     lib.yoco_ceiling_read4_write2.restype = i
     lib.yoco_ceiling_mfma_bf16.argtypes = [vp, sz, i, i, vp, vp]
@@ -54,10 +56,18 @@ def _nbytes(t: torch.Tensor) -> int:
 
 
 def yoco_ceiling_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int = 256, threads: int = 512,
-                      nontemporal: bool = True, stream=None) -> None:
+                      loads_per_thread: int = 8, nontemporal: bool = True, stream=None) -> None:
     """Read every byte of src once (see yoco_ceiling.h); sink is a device int32/uint32 [>= 1]."""
     _check(load_ceiling_library().yoco_ceiling_read(src.data_ptr(), _nbytes(src), int(workgroups), int(threads),
-                                                    int(bool(nontemporal)), sink.data_ptr(), _stream(stream)))
+                                                    int(loads_per_thread), int(bool(nontemporal)), sink.data_ptr(),
+                                                    _stream(stream)))
+
+
+def yoco_ceiling_read_blocks(src: torch.Tensor, sink: torch.Tensor, workgroups: int = 256, threads: int = 512,
+                             loads_per_thread: int = 8, stream=None) -> None:
+    """Read every byte of src once, each wavefront in contiguous blocks (see yoco_ceiling.h)."""
+    _check(load_ceiling_library().yoco_ceiling_read_blocks(src.data_ptr(), _nbytes(src), int(workgroups), int(threads),
+                                                           int(loads_per_thread), sink.data_ptr(), _stream(stream)))
 
 
 def yoco_ceiling_read4_write2(a, b, c, d, e, f, threads: int = 512, stream=None) -> None:

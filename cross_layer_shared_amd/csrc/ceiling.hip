@@ -18,7 +18,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kUnroll = 4;            // loads in flight per thread per iteration
 constexpr int kStrideWorkgroups = 2048;
 constexpr uint32_t kSinkKey = 0x9E3779B9u;
 
@@ -34,8 +33,9 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
 // Workgroup w reads vectors [w * per_wg, min((w + 1) * per_wg, n)), or, with
-// per_wg = 0, every thread strides over all n vectors.
-template <bool NT>
+// per_wg = 0, every thread strides over all n vectors; UNROLL loads of each
+// thread are in flight together.
+template <bool NT, int UNROLL>
 __global__ __launch_bounds__(1024) void read_kernel(const u32x4* __restrict__ src, uint64_t n, uint64_t per_wg,
                                                     uint32_t* __restrict__ sink) {
   const uint64_t nt = blockDim.x;
@@ -50,15 +50,38 @@ __global__ __launch_bounds__(1024) void read_kernel(const u32x4* __restrict__ sr
     step = (uint64_t)gridDim.x * nt;
   }
   uint32_t acc = 0;
-  for (uint64_t i = lo; i < hi; i += kUnroll * step) {
-    u32x4 v[kUnroll];
+  for (uint64_t i = lo; i < hi; i += UNROLL * step) {
+    u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const uint64_t k = i + u * step;
       v[u] = k < hi ? load16<NT>(src + k) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= fold(v[u]);
+    for (int u = 0; u < UNROLL; ++u) acc ^= fold(v[u]);
+  }
+  if (acc == kSinkKey) sink[0] = acc;
+}
+
+// Workgroup w reads vectors [w * per_wg, min((w + 1) * per_wg, n)) in blocks of
+// 64 UNROLL vectors (UNROLL KiB), dealt to its wavefronts in turn; a
+// wavefront's UNROLL loads of a block are in flight together, each a
+// contiguous 1 KiB, as the decode's wavefronts stream their row blocks.
+template <int UNROLL>
+__global__ __launch_bounds__(1024) void read_blocks_kernel(const u32x4* __restrict__ src, uint64_t n, uint64_t per_wg,
+                                                           uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const uint64_t lo = (uint64_t)blockIdx.x * per_wg, hi = min(lo + per_wg, n);
+  uint32_t acc = 0;
+  for (uint64_t blk = lo + (uint64_t)wave * 64 * UNROLL; blk < hi; blk += (uint64_t)waves * 64 * UNROLL) {
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const uint64_t k = blk + 64 * u + lane;
+      v[u] = k < hi ? __builtin_nontemporal_load(src + k) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc ^= fold(v[u]);
   }
   if (acc == kSinkKey) sink[0] = acc;
 }
@@ -135,29 +158,76 @@ bool overlap(const void* x, const void* y, size_t n) {
   return a < b + n && b < a + n;
 }
 
+template <int U>
+void launch_read(dim3 grid, int threads, hipStream_t stream, bool nt, const u32x4* s, uint64_t n, uint64_t per_wg,
+                 uint32_t* sink) {
+  if (nt)
+    read_kernel<true, U><<<grid, threads, 0, stream>>>(s, n, per_wg, sink);
+  else
+    read_kernel<false, U><<<grid, threads, 0, stream>>>(s, n, per_wg, sink);
+}
+
+template <int U>
+void launch_read_blocks(dim3 grid, int threads, hipStream_t stream, const u32x4* s, uint64_t n, uint64_t per_wg,
+                        uint32_t* sink) {
+  read_blocks_kernel<U><<<grid, threads, 0, stream>>>(s, n, per_wg, sink);
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* yoco_ceiling_last_error(void) { return g_err; }
 
-yoco_status yoco_ceiling_read(const void* src, size_t bytes, int workgroups, int threads, int nontemporal,
-                              uint32_t* sink, hipStream_t stream) {
+yoco_status yoco_ceiling_read(const void* src, size_t bytes, int workgroups, int threads, int loads_per_thread,
+                              int nontemporal, uint32_t* sink, hipStream_t stream) {
   if (!src || !sink) return fail(YOCO_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(src)) return fail(YOCO_ERR_ALIGNMENT, "src not 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(sink) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "sink not 4-byte aligned");
   if (bytes == 0 || bytes % 16) return fail(YOCO_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
   if (workgroups < 0 || workgroups > (1 << 20)) return fail(YOCO_ERR_INVALID_ARG, "workgroups out of range");
   if (!valid_threads(threads)) return fail(YOCO_ERR_INVALID_ARG, "threads must be 64..1024, a multiple of 64");
+  const int u = loads_per_thread;
+  if (u != 1 && u != 2 && u != 4 && u != 8 && u != 16)
+    return fail(YOCO_ERR_INVALID_ARG, "loads_per_thread must be 1, 2, 4, 8 or 16");
   const uint64_t n = bytes / 16;
   const uint64_t per_wg = workgroups ? (n + workgroups - 1) / workgroups : 0;
   const dim3 grid(workgroups ? workgroups : kStrideWorkgroups);
   const u32x4* s = static_cast<const u32x4*>(src);
-  if (nontemporal)
-    read_kernel<true><<<grid, threads, 0, stream>>>(s, n, per_wg, sink);
-  else
-    read_kernel<false><<<grid, threads, 0, stream>>>(s, n, per_wg, sink);
+  const bool nt = nontemporal != 0;
+  switch (u) {
+    case 1: launch_read<1>(grid, threads, stream, nt, s, n, per_wg, sink); break;
+    case 2: launch_read<2>(grid, threads, stream, nt, s, n, per_wg, sink); break;
+    case 4: launch_read<4>(grid, threads, stream, nt, s, n, per_wg, sink); break;
+    case 8: launch_read<8>(grid, threads, stream, nt, s, n, per_wg, sink); break;
+    default: launch_read<16>(grid, threads, stream, nt, s, n, per_wg, sink); break;
+  }
   return launched("ceiling read");
+}
+
+yoco_status yoco_ceiling_read_blocks(const void* src, size_t bytes, int workgroups, int threads, int loads_per_thread,
+                                     uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return fail(YOCO_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(src)) return fail(YOCO_ERR_ALIGNMENT, "src not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u)) return fail(YOCO_ERR_ALIGNMENT, "sink not 4-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(YOCO_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (workgroups < 1 || workgroups > (1 << 20)) return fail(YOCO_ERR_INVALID_ARG, "workgroups out of range");
+  if (!valid_threads(threads)) return fail(YOCO_ERR_INVALID_ARG, "threads must be 64..1024, a multiple of 64");
+  const int u = loads_per_thread;
+  if (u != 1 && u != 2 && u != 4 && u != 8 && u != 16)
+    return fail(YOCO_ERR_INVALID_ARG, "loads_per_thread must be 1, 2, 4, 8 or 16");
+  const uint64_t n = bytes / 16;
+  const uint64_t per_wg = (n + workgroups - 1) / workgroups;
+  const dim3 grid(workgroups);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  switch (u) {
+    case 1: launch_read_blocks<1>(grid, threads, stream, s, n, per_wg, sink); break;
+    case 2: launch_read_blocks<2>(grid, threads, stream, s, n, per_wg, sink); break;
+    case 4: launch_read_blocks<4>(grid, threads, stream, s, n, per_wg, sink); break;
+    case 8: launch_read_blocks<8>(grid, threads, stream, s, n, per_wg, sink); break;
+    default: launch_read_blocks<16>(grid, threads, stream, s, n, per_wg, sink); break;
+  }
+  return launched("ceiling read_blocks");
 }
 
 yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* c, const void* d, void* e, void* f,

@@ -37,14 +37,28 @@ extern "C" {
  *                equal ranges (the decode's split layout); 0: every thread
  *                strides over the whole buffer (grid of 2048 workgroups).
  *   threads      threads per workgroup: 64, 128, ..., 1024.
+ *   loads_per_thread  1, 2, 4, 8 or 16: the 16-byte loads of a thread issued
+ *                together before their data is used (consecutive thread
+ *                strides of the workgroup's range).
  *   nontemporal  1: nontemporal loads (the decode's policy); 0: ordinary loads
  *                (these allocate in the caches: a read of a buffer larger than
  *                the 256 MB Infinity Cache evicts what it held).
  *   sink         device uint32 [1]: written only if the XOR of all loaded
  *                words equals a fixed 32-bit constant (keeps the loads live).
  */
-yoco_status yoco_ceiling_read(const void* src, size_t bytes, int workgroups, int threads, int nontemporal,
-                              uint32_t* sink, hipStream_t stream);
+yoco_status yoco_ceiling_read(const void* src, size_t bytes, int workgroups, int threads, int loads_per_thread,
+                              int nontemporal, uint32_t* sink, hipStream_t stream);
+
+/*
+ * yoco_ceiling_read_blocks - the same single read with the decode's per-
+ * wavefront access: workgroup w reads the w-th of `workgroups` contiguous,
+ * equal ranges, dealt to its wavefronts in blocks of loads_per_thread KiB;
+ * the loads of one block (each a contiguous 1 KiB: 64 lanes x 16 bytes) are
+ * in flight together. Nontemporal loads.
+ *   workgroups   >= 1; threads and loads_per_thread as for yoco_ceiling_read.
+ */
+yoco_status yoco_ceiling_read_blocks(const void* src, size_t bytes, int workgroups, int threads, int loads_per_thread,
+                                     uint32_t* sink, hipStream_t stream);
 
 /*
  * yoco_ceiling_read4_write2 - the compose kernel's traffic with no arithmetic:

@@ -282,13 +282,21 @@ def test_ceiling_probes_reject_bad_arguments():
     lib = C.load_ceiling_library()
     sink = BASE + (1 << 30)
     cases = [
-        (lib.yoco_ceiling_read(None, 1 << 20, 256, 512, 1, sink, None), INVALID),
-        (lib.yoco_ceiling_read(BASE + 8, 1 << 20, 256, 512, 1, sink, None), ALIGN),
-        (lib.yoco_ceiling_read(BASE, 1000, 256, 512, 1, sink, None), INVALID),
-        (lib.yoco_ceiling_read(BASE, 1 << 20, -1, 512, 1, sink, None), INVALID),
-        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 100, 1, sink, None), INVALID),
-        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 2048, 1, sink, None), INVALID),
-        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 512, 1, sink + 2, None), ALIGN),
+        (lib.yoco_ceiling_read(None, 1 << 20, 256, 512, 4, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE + 8, 1 << 20, 256, 512, 4, 1, sink, None), ALIGN),
+        (lib.yoco_ceiling_read(BASE, 1000, 256, 512, 4, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, -1, 512, 4, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 100, 4, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 2048, 4, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 512, 4, 1, sink + 2, None), ALIGN),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 512, 3, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read(BASE, 1 << 20, 256, 512, 32, 1, sink, None), INVALID),
+        (lib.yoco_ceiling_read_blocks(None, 1 << 20, 256, 512, 8, sink, None), INVALID),
+        (lib.yoco_ceiling_read_blocks(BASE + 8, 1 << 20, 256, 512, 8, sink, None), ALIGN),
+        (lib.yoco_ceiling_read_blocks(BASE, 1000, 256, 512, 8, sink, None), INVALID),
+        (lib.yoco_ceiling_read_blocks(BASE, 1 << 20, 0, 512, 8, sink, None), INVALID),
+        (lib.yoco_ceiling_read_blocks(BASE, 1 << 20, 256, 100, 8, sink, None), INVALID),
+        (lib.yoco_ceiling_read_blocks(BASE, 1 << 20, 256, 512, 5, sink, None), INVALID),
     ]
     bufs = [BASE + (i << 24) for i in range(6)]
     cases += [
