@@ -652,10 +652,11 @@ def leg_ceiling(args, torch, S):
     sets = [[torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(6)] for _ in range(3)]
     nb = 6 * 2 * n
     out = {"bytes": nb, "shapes": {}}
-    for th in (256, 512, 1024):
-        fn = lambda i, th=th: C.yoco_ceiling_read4_write2(*sets[i], threads=th)  # noqa: E731
-        out["shapes"][f"{th}"] = {"hbm": rate(nb, *graph_time(torch, [lambda i=i: fn(i % 3) for i in range(6)],
-                                                              args.reps))}
+    for th, u in [(256, 1), (512, 1), (1024, 1), (256, 2), (512, 2), (256, 4)]:
+        fn = lambda i, th=th, u=u: C.yoco_ceiling_read4_write2(*sets[i], threads=th,  # noqa: E731
+                                                               positions_per_thread=u)
+        out["shapes"][f"{th}x{u}"] = {"hbm": rate(nb, *graph_time(torch, [lambda i=i: fn(i % 3) for i in range(6)],
+                                                                  args.reps))}
     out["hbm"] = best(out, "hbm")
     res["read4_write2_384MiB"] = out
     del sets

@@ -34,7 +34,7 @@ def load_ceiling_library(path: str = CEILING_LIB_PATH) -> ctypes.CDLL:
     lib.yoco_ceiling_read.restype = i
     lib.yoco_ceiling_read_blocks.argtypes = [vp, sz, i, i, i, vp, vp]
     lib.yoco_ceiling_read_blocks.restype = i
-    lib.yoco_ceiling_read4_write2.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, vp]
+    lib.yoco_ceiling_read4_write2.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, vp]
     lib.yoco_ceiling_read4_write2.restype = i
     lib.yoco_ceiling_mfma_bf16.argtypes = [vp, sz, i, i, vp, vp]
     lib.yoco_ceiling_mfma_bf16.restype = i
@@ -70,7 +70,8 @@ def yoco_ceiling_read_blocks(src: torch.Tensor, sink: torch.Tensor, workgroups: 
                                                            int(loads_per_thread), sink.data_ptr(), _stream(stream)))
 
 
-def yoco_ceiling_read4_write2(a, b, c, d, e, f, threads: int = 512, stream=None) -> None:
+def yoco_ceiling_read4_write2(a, b, c, d, e, f, threads: int = 512, positions_per_thread: int = 1,
+                              stream=None) -> None:
     """e = a + b, f = c + d as 32-bit integers; six equally sized contiguous buffers."""
     n = _nbytes(a)
     for t in (b, c, d, e, f):
@@ -78,7 +79,7 @@ def yoco_ceiling_read4_write2(a, b, c, d, e, f, threads: int = 512, stream=None)
             raise ValueError("the six buffers must have the same size")
     _check(load_ceiling_library().yoco_ceiling_read4_write2(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(),
                                                             e.data_ptr(), f.data_ptr(), n, int(threads),
-                                                            _stream(stream)))
+                                                            int(positions_per_thread), _stream(stream)))
 
 
 MFMA_THREADS = 512

@@ -86,15 +86,32 @@ __global__ __launch_bounds__(1024) void read_blocks_kernel(const u32x4* __restri
   if (acc == kSinkKey) sink[0] = acc;
 }
 
+// U positions per thread, blockDim apart (each load and store instruction of a
+// wavefront stays one contiguous 1 KiB); every load is issued before any store.
+template <int U>
 __global__ __launch_bounds__(1024) void read4_write2_kernel(const u32x4* __restrict__ a, const u32x4* __restrict__ b,
                                                             const u32x4* __restrict__ c, const u32x4* __restrict__ d,
                                                             u32x4* __restrict__ e, u32x4* __restrict__ f, uint64_t n) {
-  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const u32x4 va = __builtin_nontemporal_load(a + i), vb = __builtin_nontemporal_load(b + i);
-  const u32x4 vc = __builtin_nontemporal_load(c + i), vd = __builtin_nontemporal_load(d + i);
-  __builtin_nontemporal_store(va + vb, e + i);
-  __builtin_nontemporal_store(vc + vd, f + i);
+  const uint64_t base = (uint64_t)blockIdx.x * blockDim.x * U + threadIdx.x;
+  u32x4 va[U], vb[U], vc[U], vd[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t i = base + (uint64_t)u * blockDim.x;
+    if (i < n) {
+      va[u] = __builtin_nontemporal_load(a + i);
+      vb[u] = __builtin_nontemporal_load(b + i);
+      vc[u] = __builtin_nontemporal_load(c + i);
+      vd[u] = __builtin_nontemporal_load(d + i);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t i = base + (uint64_t)u * blockDim.x;
+    if (i < n) {
+      __builtin_nontemporal_store(va[u] + vb[u], e + i);
+      __builtin_nontemporal_store(vc[u] + vd[u], f + i);
+    }
+  }
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -231,7 +248,7 @@ yoco_status yoco_ceiling_read_blocks(const void* src, size_t bytes, int workgrou
 }
 
 yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* c, const void* d, void* e, void* f,
-                                      size_t bytes, int threads, hipStream_t stream) {
+                                      size_t bytes, int threads, int positions_per_thread, hipStream_t stream) {
   const void* ins[4] = {a, b, c, d};
   void* outs[2] = {e, f};
   for (const void* p : ins)
@@ -245,15 +262,24 @@ yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* 
   if (bytes == 0 || bytes % 16 || bytes >= (1ull << 35))
     return fail(YOCO_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 below 2^35");
   if (!valid_threads(threads)) return fail(YOCO_ERR_INVALID_ARG, "threads must be 64..1024, a multiple of 64");
+  const int u = positions_per_thread;
+  if (u != 1 && u != 2 && u != 4) return fail(YOCO_ERR_INVALID_ARG, "positions_per_thread must be 1, 2 or 4");
   for (void* o : outs)
     for (const void* p : ins)
       if (overlap(o, p, bytes)) return fail(YOCO_ERR_INVALID_ARG, "a destination overlaps a source");
   if (overlap(e, f, bytes)) return fail(YOCO_ERR_INVALID_ARG, "the destinations overlap");
   const uint64_t n = bytes / 16;
-  const dim3 grid((unsigned)((n + threads - 1) / threads));
-  read4_write2_kernel<<<grid, threads, 0, stream>>>(
-      static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), static_cast<const u32x4*>(c),
-      static_cast<const u32x4*>(d), static_cast<u32x4*>(e), static_cast<u32x4*>(f), n);
+  const uint64_t per_wg = (uint64_t)threads * u;
+  const dim3 grid((unsigned)((n + per_wg - 1) / per_wg));
+  const u32x4 *pa = static_cast<const u32x4*>(a), *pb = static_cast<const u32x4*>(b);
+  const u32x4 *pc = static_cast<const u32x4*>(c), *pd = static_cast<const u32x4*>(d);
+  u32x4 *pe = static_cast<u32x4*>(e), *pf = static_cast<u32x4*>(f);
+  if (u == 1)
+    read4_write2_kernel<1><<<grid, threads, 0, stream>>>(pa, pb, pc, pd, pe, pf, n);
+  else if (u == 2)
+    read4_write2_kernel<2><<<grid, threads, 0, stream>>>(pa, pb, pc, pd, pe, pf, n);
+  else
+    read4_write2_kernel<4><<<grid, threads, 0, stream>>>(pa, pb, pc, pd, pe, pf, n);
   return launched("ceiling read4_write2");
 }
 

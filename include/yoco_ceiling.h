@@ -63,13 +63,15 @@ yoco_status yoco_ceiling_read_blocks(const void* src, size_t bytes, int workgrou
 /*
  * yoco_ceiling_read4_write2 - the compose kernel's traffic with no arithmetic:
  * e = a + b and f = c + d as 32-bit integers over `bytes` bytes per stream,
- * one 16-byte vector of each stream per thread, nontemporal loads and stores.
+ * 16-byte vectors, nontemporal loads and stores.
  *   a, b, c, d   sources; e, f destinations (must not overlap the sources).
  *   bytes        bytes per stream, a positive multiple of 16, below 2^35.
  *   threads      threads per workgroup: 64, 128, ..., 1024.
+ *   positions_per_thread  1, 2 or 4 vectors of each stream per thread, a
+ *                workgroup's width apart; all loads before the stores.
  */
 yoco_status yoco_ceiling_read4_write2(const void* a, const void* b, const void* c, const void* d, void* e, void* f,
-                                      size_t bytes, int threads, hipStream_t stream);
+                                      size_t bytes, int threads, int positions_per_thread, hipStream_t stream);
 
 /*
  * yoco_ceiling_mfma_bf16 - the matrix cores' achievable rate on given operand

@@ -300,12 +300,13 @@ def test_ceiling_probes_reject_bad_arguments():
     ]
     bufs = [BASE + (i << 24) for i in range(6)]
     cases += [
-        (lib.yoco_ceiling_read4_write2(*bufs[:5], None, 1 << 20, 512, None), INVALID),
-        (lib.yoco_ceiling_read4_write2(*bufs[:5], bufs[5] + 4, 1 << 20, 512, None), ALIGN),
-        (lib.yoco_ceiling_read4_write2(*bufs, 0, 512, None), INVALID),
-        (lib.yoco_ceiling_read4_write2(*bufs, 1 << 20, 32, None), INVALID),
-        (lib.yoco_ceiling_read4_write2(*bufs[:4], bufs[0], bufs[5], 1 << 20, 512, None), INVALID),   # e aliases a
-        (lib.yoco_ceiling_read4_write2(*bufs[:5], bufs[4] + 16, 1 << 20, 512, None), INVALID),       # e, f overlap
+        (lib.yoco_ceiling_read4_write2(*bufs[:5], None, 1 << 20, 512, 1, None), INVALID),
+        (lib.yoco_ceiling_read4_write2(*bufs[:5], bufs[5] + 4, 1 << 20, 512, 1, None), ALIGN),
+        (lib.yoco_ceiling_read4_write2(*bufs, 0, 512, 1, None), INVALID),
+        (lib.yoco_ceiling_read4_write2(*bufs, 1 << 20, 32, 1, None), INVALID),
+        (lib.yoco_ceiling_read4_write2(*bufs[:4], bufs[0], bufs[5], 1 << 20, 512, 1, None), INVALID),   # e aliases a
+        (lib.yoco_ceiling_read4_write2(*bufs[:5], bufs[4] + 16, 1 << 20, 512, 1, None), INVALID),       # e, f overlap
+        (lib.yoco_ceiling_read4_write2(*bufs, 1 << 20, 512, 3, None), INVALID),
     ]
     cases += [
         (lib.yoco_ceiling_mfma_bf16(None, 1 << 20, 256, 16, sink, None), INVALID),
