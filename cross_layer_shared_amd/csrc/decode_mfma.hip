@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 
 #include "decode_kernel.h"
+#include "decode_layout.h"
 
 namespace yoco {
 namespace {
@@ -58,16 +59,6 @@ constexpr float kLazy = 8.f;     // rescale threshold of the running max (log2 u
 __device__ __forceinline__ s16x4_t read_tr16(const __bf16* ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4_t*)(__attribute__((address_space(3))) void*)(const_cast<__bf16*>(ptr)));
-}
-
-// LDS position of 16-byte chunk c of K row r (r < 32) in a wavefront's K
-// buffer: c ^ k_swizzle(r). The 16 rows a score operand read serves,
-// 8 (i / 4) + 4 bb + (i % 4), i < 16, then land in distinct banks (distinct
-// chunk positions of a 256-byte row at D = 128; distinct (row parity, chunk)
-// pairs at D = 64), and so do the 16 lanes of a row-contiguous write.
-template <int D>
-__host__ __device__ constexpr int k_swizzle(int r) {
-  return D == 128 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | ((r >> 2) & 6));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -95,12 +86,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   constexpr bool APP = MODE == kAppend;          // self-decoder step: compose and append the new row
   constexpr int NQK = D / 32;          // k-steps of the score product
   constexpr int NDB = D / 16;          // 16-dim blocks of O^T
-  constexpr int VPAD = D + 32;         // LDS row stride of a V block (bf16); conflict-free transposing reads
-  constexpr int LPR = D / 8;           // lanes per cache row in the V block loads (16 bytes each)
-  constexpr int RPI = 64 / LPR;        // cache rows per V load instruction
-  constexpr int NVI = kBlock / RPI;    // V load instructions per block
-  constexpr int SV = NW * kBlock * VPAD * 2;          // bytes of the per-wavefront V buffers
-  constexpr int SK = NW * kBlock * D * 2;             // bytes of the per-wavefront K buffers
+  // per-wavefront LDS buffers and their addresses: decode_layout.h (checked by a host build)
+  using L = dlay::Shape<D>;
+  constexpr int RPI = L::RPI;          // cache rows per load instruction (L::LPR lanes per row, 16 bytes each)
+  constexpr int NVI = L::NLI;          // load instructions per block and tensor
+  constexpr int SV = NW * L::kVElems * 2;             // bytes of the per-wavefront V buffers
+  constexpr int SK = NW * L::kKElems * 2;             // bytes of the per-wavefront K buffers
   constexpr int SM = NW * G * (D + 2) * 4;            // bytes of the wavefront merge
   __shared__ __attribute__((aligned(16))) unsigned char smem[SV + SK > SM ? SV + SK : SM];
 
@@ -160,9 +151,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
                             te > 0 ? (uint32_t)te * kst : 0u);
   const auto rv = rows_rsrc(static_cast<const char*>(p.v.ptr) + ((int64_t)b * p.v.sb + (int64_t)g * p.v.sh) * 2,
                             te > 0 ? (uint32_t)te * vst : 0u);
-  // Block loads: instruction i brings rows RPI i .. + RPI, lane -> row lane / LPR, dims 8 (lane % LPR).
-  const uint32_t koff = (uint32_t)(lane / LPR) * kst + 16u * (lane % LPR);
-  const uint32_t voff = (uint32_t)(lane / LPR) * vst + 16u * (lane % LPR);
+  // Block loads: instruction i brings rows RPI i .. + RPI, lane -> row lane / L::LPR, dims 8 (lane % L::LPR).
+  const uint32_t koff = (uint32_t)dlay::load_row<D>(0, lane) * kst + 16u * dlay::load_chunk<D>(lane);
+  const uint32_t voff = (uint32_t)dlay::load_row<D>(0, lane) * vst + 16u * dlay::load_chunk<D>(lane);
 
   auto load = [&](int base, u32x4_t (&kr)[NVI], u32x4_t (&vr)[NVI]) {
 #pragma unroll
@@ -184,8 +175,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
                     te > 0 ? (uint32_t)te * k1st : 0u);
     rv1 = rows_rsrc(static_cast<const char*>(p.v1.ptr) + ((int64_t)b * p.v1.sb + (int64_t)g * p.v1.sh) * 2,
                     te > 0 ? (uint32_t)te * v1st : 0u);
-    koff1 = (uint32_t)(lane / LPR) * k1st + 16u * (lane % LPR);
-    voff1 = (uint32_t)(lane / LPR) * v1st + 16u * (lane % LPR);
+    koff1 = (uint32_t)dlay::load_row<D>(0, lane) * k1st + 16u * dlay::load_chunk<D>(lane);
+    voff1 = (uint32_t)dlay::load_row<D>(0, lane) * v1st + 16u * dlay::load_chunk<D>(lane);
   }
   auto compose4 = [&](u32x4_t x1, u32x4_t xi, float c1, float c2, int terms) {
     u32x4_t r;
@@ -206,15 +197,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
     for (int i = 0; i < NVI; ++i) vr[i] = compose4(v1r[i], vr[i], p.cV1, p.cV2, p.termsV);
   };
 
-  __bf16* sv = reinterpret_cast<__bf16*>(smem) + wave * kBlock * VPAD;
-  const __bf16* tr0 = sv + (8 * lg + (lr >> 2)) * VPAD + 4 * (lr & 3);   // rows 8 lg + 0..3 of this lane's reads
+  __bf16* sv = reinterpret_cast<__bf16*>(smem) + wave * L::kVElems;
   // this wavefront's K buffer: kBlock rows of D, chunk c of row r at position c ^ k_swizzle(r)
-  __bf16* sk = reinterpret_cast<__bf16*>(smem + SV) + wave * kBlock * D;
-  const int krow_w = lane / LPR, kchunk_w = lane % LPR;   // what this lane's block loads carry: row RPI i + krow_w
-  // score operand of block bb, k-step j: row 8 (lr / 4) + 4 bb + lr % 4, chunk 4 j + lg
-  int krd[2];
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) krd[bb] = (8 * (lr >> 2) + 4 * bb + (lr & 3)) * D;
+  __bf16* sk = reinterpret_cast<__bf16*>(smem + SV) + wave * L::kKElems;
   f32x4_t o[NDB];
 #pragma unroll
   for (int n = 0; n < NDB; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -225,23 +210,18 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   auto block = [&](const u32x4_t (&kr)[NVI], const u32x4_t (&vr)[NVI], int base) {
     // K and V rows into this wavefront's LDS buffers (K swizzled, V padded rows)
 #pragma unroll
-    for (int i = 0; i < NVI; ++i) {
-      const int r = RPI * i + krow_w;
-      *reinterpret_cast<u32x4_t*>(sk + r * D + 8 * (kchunk_w ^ k_swizzle<D>(r))) = kr[i];
-    }
+    for (int i = 0; i < NVI; ++i) *reinterpret_cast<u32x4_t*>(sk + dlay::k_write<D>(i, lane)) = kr[i];
 #pragma unroll
-    for (int i = 0; i < NVI; ++i)
-      *reinterpret_cast<u32x4_t*>(sv + (RPI * i + lane / LPR) * VPAD + 8 * (lane % LPR)) = vr[i];
+    for (int i = 0; i < NVI; ++i) *reinterpret_cast<u32x4_t*>(sv + dlay::v_write<D>(i, lane)) = vr[i];
     __builtin_amdgcn_wave_barrier();
     // S^T: lane (lg, q) gets the raw scores of query q for rows 8 lg + 4 bb + i
     f32x4_t sc[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      const int r = 8 * (lr >> 2) + 4 * bb + (lr & 3);
       sc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NQK; ++j) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(sk + krd[bb] + 8 * ((4 * j + lg) ^ k_swizzle<D>(r)));
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(sk + dlay::k_read<D>(lane, bb, j));
         sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[j], sc[bb], 0, 0, 0);
       }
     }
@@ -283,8 +263,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int n = 0; n < NDB; ++n) {
-      const s16x4_t r0 = read_tr16(tr0 + 16 * n);
-      const s16x4_t r1 = read_tr16(tr0 + 4 * VPAD + 16 * n);
+      const s16x4_t r0 = read_tr16(sv + dlay::v_tr_read<D>(lane, n, 0));
+      const s16x4_t r1 = read_tr16(sv + dlay::v_tr_read<D>(lane, n, 1));
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
       o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, o[n], 0, 0, 0);
       o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, o[n], 0, 0, 0);

@@ -5,8 +5,9 @@
 // and dims its lane must supply (lane l of v_mfma_f32_32x32x16_bf16 supplies
 // A[l % 32][8 (l / 32) .. + 8]), that every access stays inside its slot and
 // the 150 KiB array, and that the reads the kernel relies on touch every LDS
-// bank once per group of lanes served together (64 banks of 4 bytes: 16 lanes
-// for 16-byte reads, 32 lanes for 8-byte reads). The transposing read is
+// bank once per group of lanes (64 banks of 4 bytes: 16 lanes for the 16-byte
+// reads; the 8-byte transposing reads over 32 lanes, more than the LDS needs,
+// since it serves them 16 lanes at a time). The transposing read is
 // modelled as the kernel comments state it: within a 16-lane group, lanes
 // 4a .. 4a + 3 address row a (4 dims each) and lane i receives element i of
 // every row.

@@ -11,7 +11,10 @@
   tests/host_build/prefill_layout_check.cpp): slot bounds, that the direct
   loads fill each tile once, that each MFMA operand read finds the rows and
   dims its lane supplies, and the bank-conflict-free reads; planted mistakes in
-  a copy of the layout make that check fail.
+  a copy of the layout make that check fail;
+- the same for the matrix-core decode's per-wavefront K and V buffers
+  (decode_layout.h, through tests/host_build/decode_layout_check.cpp), at
+  D = 128 and 64.
 
 The host compiler is g++ (the C ABI layer includes only the HIP runtime's API
 header), so no device code is built here."""
@@ -81,6 +84,39 @@ def test_prefill_lds_address_check_rejects_planted_mistakes(tmp_path, name):
     (tmp_path / "prefill_layout.h").write_text(text.replace(old, new))
     src = tmp_path / "prefill_layout_check.cpp"     # next to the mutated header, which it then includes
     src.write_text(open(os.path.join(HERE, "prefill_layout_check.cpp")).read())
+    exe = str(tmp_path / "check")
+    r = subprocess.run(["g++", *COMMON, "-O1", str(src), "-o", exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert run.returncode != 0 and "FAIL" in run.stdout, f"{name}: not detected\n{run.stdout[-1000:]}"
+
+
+def test_decode_lds_addresses(tmp_path):
+    _build_and_run(tmp_path, "decode_layout_check", [os.path.join(HERE, "decode_layout_check.cpp")],
+                   ["-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"])
+
+
+DECODE_LAYOUT_MUTATIONS = {
+    "K rows stored without their swizzle": ("8 * (load_chunk<D>(lane) ^ k_swizzle<D>(load_row<D>(i, lane)))",
+                                            "8 * load_chunk<D>(lane)"),
+    "score operand chunk not swizzled": ("8 * ((4 * j + (lane >> 4)) ^ k_swizzle<D>(k_row<D>(lane, bb)))",
+                                         "8 * (4 * j + (lane >> 4))"),
+    "score operand rows in plain order": ("return 8 * ((lane & 15) >> 2) + 4 * bb + (lane & 3);",
+                                          "return (lane & 15) + 16 * bb;"),
+    "transposing read of the wrong row quad": ("(8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2))",
+                                               "(8 * (lane >> 4) + 4 * (1 - h) + ((lane & 15) >> 2))"),
+    "V rows without their pad": ("static constexpr int VPAD = D + 32;", "static constexpr int VPAD = D;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_LAYOUT_MUTATIONS))
+def test_decode_lds_address_check_rejects_planted_mistakes(tmp_path, name):
+    old, new = DECODE_LAYOUT_MUTATIONS[name]
+    text = open(os.path.join(CSRC, "decode_layout.h")).read()
+    assert text.count(old) == 1, old
+    (tmp_path / "decode_layout.h").write_text(text.replace(old, new))
+    src = tmp_path / "decode_layout_check.cpp"
+    src.write_text(open(os.path.join(HERE, "decode_layout_check.cpp")).read())
     exe = str(tmp_path / "check")
     r = subprocess.run(["g++", *COMMON, "-O1", str(src), "-o", exe], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
