@@ -98,6 +98,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
+  // Kernel arguments in one batch: the query pointer and the cache views the
+  // first row loads need are held in registers here, ahead of the branches
+  // below; left to the compiler they are fetched in a second round trip after
+  // the first batch, and every launch pays it before its stream starts.
+  asm volatile("" ::"s"(p.q), "s"(p.k.ptr), "s"(p.k.sb), "s"(p.k.sh), "s"(p.k.st), "s"(p.v.ptr), "s"(p.v.sb),
+               "s"(p.v.sh), "s"(p.v.st));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lg = lane >> 4;            // 16-lane row of the MFMA operands
